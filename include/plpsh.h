@@ -1,0 +1,227 @@
+/*
+ * plpsh.h -- C ABI of the Positional-LSH approximation of ALiBi attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method.  The explainer pages of arXiv 2605.09472,
+ * "Positional LSH: Binary Block Matrix Approximation for Attention with
+ * Linear Biases" (D. Wolfson, T. Wagner; gist.science, Dutch / Chinese /
+ * Japanese versions with the same sections).  Citations below name the
+ * section of those pages: "Methodology 1" (positional LSH framework),
+ * "Theorem 2.1" (structural approximation), "Theorem 2.2" (algorithmic
+ * reduction), "Key results".
+ *
+ * What is computed.  ALiBi attention with slope 1/sigma weights key j of
+ * query r by L*[r,j] = exp(-|r-j|/sigma), a Laplace kernel over positions
+ * (Methodology 1).  A random-binning hash of the integer positions --
+ * width delta ~ Gamma(shape 2, scale sigma), offset u ~ U[0, delta),
+ * bin(x) = floor((x - u) / delta) -- cuts [0, n) into contiguous,
+ * non-overlapping blocks, and E[M(h)] = L* for its block mask M(h)
+ * (Methodology 1).  With s i.i.d. hashes the empirical mean
+ * M~ = (1/s) sum_i M(h_i) approximates L* (Theorem 2.1), and
+ *
+ *   O_r = sum_j c[r,j] C[r,j] exp(S[r,j]) v_j / sum_j c[r,j] C[r,j] exp(S[r,j])
+ *
+ * with c[r,j] = #{i : bin_i(r) == bin_i(j)} = s * M~[r,j],
+ * S = Q K^T / sqrt(d) and C[r,j] = [j <= r] when causal (else 1), is the
+ * attention with L* replaced by M~ (Theorem 2.1, Theorem 2.2).
+ *
+ * Conventions shared by every entry point.
+ *  - Every function returns a plpsh_status, never throws and never exits.
+ *  - Every argument is validated before any HIP call; on a validation error
+ *    nothing is launched and no output is touched.
+ *  - Device pointers are caller-owned device memory (e.g. PyTorch tensors);
+ *    the library allocates no device memory.  Host pointers are only read
+ *    or written during the call.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Device work is
+ *    enqueued on it and runs asynchronously; results are valid after the
+ *    caller synchronises the stream.  PLPSH_ERR_HIP reports a launch or
+ *    runtime error returned by HIP during the call; asynchronous device
+ *    faults surface at the caller's next synchronisation.
+ *  - Work runs on the calling thread's current HIP device.
+ *  - Entry points are reentrant.  The library keeps, per device, a small
+ *    pinned host staging ring for hash parameters (allocated on first use,
+ *    held until process exit).
+ */
+#ifndef PLPSH_H
+#define PLPSH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PLPSH_OK = 0,
+    PLPSH_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, bad value */
+    PLPSH_ERR_UNSUPPORTED = 2,        /* valid but not implemented (e.g. head_dim) */
+    PLPSH_ERR_WORKSPACE_TOO_SMALL = 3,
+    PLPSH_ERR_HIP = 4                 /* HIP runtime / launch error */
+} plpsh_status;
+
+typedef enum {
+    PLPSH_DTYPE_F32 = 0,    /* float32 Q/K/V/O; fp32 matrix cores, fp32 softmax */
+    PLPSH_DTYPE_BF16 = 1    /* bfloat16 Q/K/V/O; bf16 matrix cores, fp32 accumulation */
+} plpsh_dtype;
+
+/* Limits of this implementation. */
+#define PLPSH_MAX_S 128            /* hashes per head */
+#define PLPSH_MAX_N 524288         /* sequence length */
+#define PLPSH_MAX_HASHES 65536     /* heads * s per call */
+#define PLPSH_PLAN_TILE 128        /* query rows per plan record */
+
+/* Human-readable name of a status code (static storage). */
+const char* plpsh_status_string(plpsh_status st);
+
+/* Library version string (static storage). */
+const char* plpsh_version(void);
+
+/* Description of the HIP failure behind the most recent PLPSH_ERR_HIP
+ * returned on the calling thread ("" if none): the failing HIP call and
+ * hipGetErrorString of its result.  Thread-local storage, valid until the
+ * thread's next call into the library. */
+const char* plpsh_last_hip_error(void);
+
+/*
+ * plpsh_draw_hashes -- draw the random-binning hashes on the host.
+ *
+ * The hash law is the random binning of Rahimi and Recht for the Laplace
+ * kernel exp(-|x-y|/sigma) applied to integer positions (Methodology 1); its
+ * width follows a Gamma distribution (Theorem 2.1, tools of the proof):
+ * delta ~ Gamma(shape 2, scale sigma_h), u ~ U[0, delta).  Draws are
+ * independent per (head h, hash i) and do not depend on Q, K, V, as the
+ * uniform guarantee of Theorem 2.2 requires.
+ *
+ * Generator (exact, bit-reproducible): SplitMix64 (Steele, Lea, Flood,
+ * OOPSLA 2014) in counter mode.  For k in {0,1,2}:
+ *   c_k   = (h << 32) | (i << 2) | k
+ *   z_k   = mix64(seed + (c_k + 1) * 0x9E3779B97F4A7C15)  (mod 2^64)
+ *   mix64(z): z = (z ^ z>>30) * 0xBF58476D1CE4E5B9;
+ *             z = (z ^ z>>27) * 0x94D049BB133111EB;  return z ^ z>>31
+ *   U_k   = ((z_k >> 12) + 0.5) * 2^-52                  (0 < U_k < 1, exact)
+ *   delta = sigma_h * ((-log U_0) - log U_1)            (binary64, this order)
+ *   u     = delta * U_2
+ * with log the C library's natural logarithm.
+ *
+ *   seed   : any 64-bit value.
+ *   heads  : >= 1; s: 1..PLPSH_MAX_S; heads * s <= PLPSH_MAX_HASHES.
+ *   sigma  : host [heads], finite, > 0 (sigma_h = 1 / ALiBi slope of head h).
+ *   delta,u: host out [heads * s], index h * s + i; caller-owned.
+ * Errors: INVALID_ARGUMENT for null pointers or out-of-range values.
+ */
+plpsh_status plpsh_draw_hashes(uint64_t seed, int32_t heads, int32_t s,
+                               const double* sigma, double* delta, double* u);
+
+/*
+ * Bin buffer: the device-side description of the blocks of every hash,
+ * computed from (delta, u) by the bin kernel.  Layout (byte offsets from
+ * plpsh_bins_layout, each 256-byte aligned), for H = heads hashes-owners,
+ * hash index t = h * s + i, T = ceil(n / PLPSH_PLAN_TILE):
+ *
+ *   nblk  : int32 [H*s]            number of blocks of hash t
+ *   starts: int32 [H*s][n+1]       starts[t][k] = first position of block k
+ *                                  (k < nblk[t]); starts[t][nblk[t]] = n.
+ *                                  Entries beyond are unspecified.
+ *                                  (The "int32 prefix offsets" of the bins.)
+ *   plan  : record [H][T][s], 32 bytes each, for query tile
+ *           [128 q, 128 q + 128) of head h and hash i:
+ *             int32 a, e    block [a, e) containing row 128 q
+ *             int32 a2, e2  block containing row min(128 q + 127, n - 1)
+ *             uint32 bits[4] bit p set iff position 128 q + p (1 <= p < 128)
+ *                            starts a block, or equals n
+ *
+ * Block k of hash t is the maximal run of positions with equal bin value
+ * floor((x - u) / delta) evaluated in IEEE binary64 (Methodology 1: bins of
+ * the integer indices are contiguous and non-overlapping).  Block starts are
+ * bit-exact functions of (delta, u, n).
+ */
+size_t plpsh_bins_bytes(int32_t heads, int32_t s, int32_t n);
+plpsh_status plpsh_bins_layout(int32_t heads, int32_t s, int32_t n,
+                               size_t* off_nblk, size_t* off_starts, size_t* off_plan);
+
+/*
+ * plpsh_sample_bins -- draw hashes on the host (as plpsh_draw_hashes) and,
+ * if `bins` is not NULL, compute the bin buffer on the device.
+ *
+ *   delta, u   : host out [heads*s] or NULL.
+ *   bins       : device out, plpsh_bins_bytes(heads, s, n) bytes, or NULL.
+ *   n          : 1..PLPSH_MAX_N (only used when bins != NULL).
+ * Errors: INVALID_ARGUMENT (as above; bins_bytes too small counts as
+ * WORKSPACE_TOO_SMALL), HIP.
+ */
+plpsh_status plpsh_sample_bins(uint64_t seed, int32_t heads, int32_t s, int32_t n,
+                               const double* sigma, double* delta, double* u,
+                               void* bins, size_t bins_bytes, void* stream);
+
+/*
+ * plpsh_bins_from_hashes -- the device bin kernel for explicit hashes.
+ *   delta, u : host [heads*s]; delta finite and > 0; 0 <= u <= delta.
+ */
+plpsh_status plpsh_bins_from_hashes(int32_t heads, int32_t s, int32_t n,
+                                    const double* delta, const double* u,
+                                    void* bins, size_t bins_bytes, void* stream);
+
+/* Workspace bytes needed by plpsh_attention_fwd[_hashes] (= bin buffer). */
+size_t plpsh_workspace_bytes(int32_t heads_q, int32_t s, int32_t n);
+
+/*
+ * plpsh_attention_fwd -- Positional-LSH ALiBi attention, forward pass
+ * (Theorem 2.2 with M~ of Theorem 2.1).  Draws s hashes per query head from
+ * `seed` on the host, computes their blocks on the device, then
+ * O = count-weighted attention (formula at the top of this file).
+ *
+ *   q, o     : device [batch, heads_q,  n, head_dim], contiguous, d innermost
+ *   k, v     : device [batch, heads_kv, n, head_dim], contiguous
+ *              All 16-byte aligned; o must not alias q, k or v.
+ *              Query head h reads key/value head h / (heads_q / heads_kv).
+ *   dtype    : element type of q, k, v and o.
+ *   head_dim : 64 or 128 (else UNSUPPORTED).  Scale 1/sqrt(head_dim).
+ *   sigma    : host [heads_q], finite, > 0.
+ *   s        : 1..PLPSH_MAX_S hashes per head, shared by all batch rows.
+ *   causal   : 0 or 1; 1 multiplies the mask elementwise by [j <= r].
+ *   workspace: device, >= plpsh_workspace_bytes(heads_q, s, n) bytes,
+ *              256-byte aligned; overwritten.
+ * batch == 0 or n == 0 is a valid empty call: nothing is launched and
+ * q, k, v, o may then be NULL.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP.
+ */
+plpsh_status plpsh_attention_fwd(const void* q, const void* k, const void* v, void* o,
+                                 int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                 int32_t n, int32_t head_dim, plpsh_dtype dtype,
+                                 const double* sigma, int32_t s, uint64_t seed,
+                                 int32_t causal, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
+ * plpsh_attention_fwd_hashes -- as plpsh_attention_fwd with explicit hashes
+ * instead of a seed: delta, u host [heads_q * s] (index h * s + i), delta
+ * finite > 0, 0 <= u <= delta.  Lets a caller reuse a draw or force special
+ * cases (delta >= n: one block, plain attention; delta < 1: single-position
+ * blocks, O = V).
+ */
+plpsh_status plpsh_attention_fwd_hashes(const void* q, const void* k, const void* v, void* o,
+                                        int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                        int32_t n, int32_t head_dim, plpsh_dtype dtype,
+                                        const double* delta, const double* u, int32_t s,
+                                        int32_t causal, void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
+/*
+ * plpsh_alibi_dense_fwd -- exact ALiBi attention T* (the quantity the
+ * approximation targets, Methodology 1), dense over all keys:
+ *   O_r = sum_j C[r,j] exp(S[r,j] - |r-j|/sigma_h) v_j / sum_j (same weights)
+ * Same layouts, dtypes, head_dim values and error conventions as
+ * plpsh_attention_fwd; needs no workspace.  Provided to locate the sequence
+ * length where the approximation overtakes exact attention on the same GPU.
+ */
+plpsh_status plpsh_alibi_dense_fwd(const void* q, const void* k, const void* v, void* o,
+                                   int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                   int32_t n, int32_t head_dim, plpsh_dtype dtype,
+                                   const double* sigma, int32_t causal, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PLPSH_H */

@@ -1,0 +1,23 @@
+"""Positional-LSH approximation of ALiBi attention on AMD MI355X (gfx950).
+
+The computation runs in hand-written HIP kernels behind the C ABI of
+``libplpsh.so`` (``include/plpsh.h``); this package only marshals
+arguments.  See ``_binding`` for the functions.
+"""
+
+from ._binding import (  # noqa: F401
+    LIB_PATH,
+    Bins,
+    PlpshError,
+    alibi_dense,
+    attention,
+    attention_hashes,
+    bins_from_hashes,
+    bins_layout,
+    draw_hashes,
+    raw,
+    sample_bins,
+    status_string,
+    version,
+    workspace_bytes,
+)

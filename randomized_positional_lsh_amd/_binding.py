@@ -1,0 +1,254 @@
+"""ctypes binding of libplpsh (C ABI in include/plpsh.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libplpsh.so.  PyTorch supplies device memory and the stream.
+If the library has not been built the import fails loudly; there is no
+fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libplpsh.so")
+
+OK = 0
+INVALID_ARGUMENT = 1
+UNSUPPORTED = 2
+WORKSPACE_TOO_SMALL = 3
+HIP_ERROR = 4
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+MAX_S = 128
+MAX_N = 524288
+PLAN_TILE = 128
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python randomized_positional_lsh_amd/build.py` "
+        "(hipcc, gfx950). There is no fallback implementation.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_c_int = ctypes.c_int32
+_c_sz = ctypes.c_size_t
+_vp = ctypes.c_void_p
+_dp = ctypes.POINTER(ctypes.c_double)
+_szp = ctypes.POINTER(ctypes.c_size_t)
+
+_SIGS = {
+    "plpsh_status_string": (ctypes.c_char_p, [_c_int]),
+    "plpsh_version": (ctypes.c_char_p, []),
+    "plpsh_last_hip_error": (ctypes.c_char_p, []),
+    "plpsh_draw_hashes": (_c_int, [ctypes.c_uint64, _c_int, _c_int, _dp, _dp, _dp]),
+    "plpsh_bins_bytes": (_c_sz, [_c_int, _c_int, _c_int]),
+    "plpsh_bins_layout": (_c_int, [_c_int, _c_int, _c_int, _szp, _szp, _szp]),
+    "plpsh_sample_bins": (_c_int, [ctypes.c_uint64, _c_int, _c_int, _c_int, _dp, _dp, _dp, _vp, _c_sz, _vp]),
+    "plpsh_bins_from_hashes": (_c_int, [_c_int, _c_int, _c_int, _dp, _dp, _vp, _c_sz, _vp]),
+    "plpsh_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int]),
+    "plpsh_attention_fwd": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                     _dp, _c_int, ctypes.c_uint64, _c_int, _vp, _c_sz, _vp]),
+    "plpsh_attention_fwd_hashes": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                            _dp, _dp, _c_int, _c_int, _vp, _c_sz, _vp]),
+    "plpsh_alibi_dense_fwd": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                       _dp, _c_int, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+class PlpshError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = f"{where}: {status_string(status)}"
+        if status == HIP_ERROR:
+            msg += f" [{_lib.plpsh_last_hip_error().decode()}]"
+        super().__init__(msg)
+
+
+def status_string(status: int) -> str:
+    return _lib.plpsh_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return _lib.plpsh_version().decode()
+
+
+def raw():
+    """The ctypes library handle (for tests of the C ABI itself)."""
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_dp)
+
+
+def _check(st: int, where: str):
+    if st != OK:
+        raise PlpshError(st, where)
+
+
+def draw_hashes(seed: int, sigma, s: int) -> tuple[np.ndarray, np.ndarray]:
+    """Host draw of (delta, u), each float64 [H, s] (plpsh_draw_hashes)."""
+    sig = _f64(sigma).reshape(-1)
+    H = sig.size
+    delta = np.empty((H, s))
+    u = np.empty((H, s))
+    _check(_lib.plpsh_draw_hashes(ctypes.c_uint64(seed & (2 ** 64 - 1)), H, s, _ptr(sig), _ptr(delta), _ptr(u)),
+           "plpsh_draw_hashes")
+    return delta, u
+
+
+def bins_layout(heads: int, s: int, n: int) -> dict:
+    a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(_lib.plpsh_bins_layout(heads, s, n, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)),
+           "plpsh_bins_layout")
+    return {"nblk": a.value, "starts": b.value, "plan": c.value, "total": _lib.plpsh_bins_bytes(heads, s, n)}
+
+
+def workspace_bytes(heads_q: int, s: int, n: int) -> int:
+    return int(_lib.plpsh_workspace_bytes(heads_q, s, n))
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _torch_dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
+
+
+class Bins:
+    """Views of a device bin buffer (layout of plpsh.h)."""
+
+    def __init__(self, buf, heads: int, s: int, n: int):
+        import torch
+        L = bins_layout(heads, s, n)
+        self.buffer, self.heads, self.s, self.n = buf, heads, s, n
+        hs = heads * s
+        b8 = buf.view(torch.uint8)
+        self.nblk = b8[L["nblk"]:L["nblk"] + 4 * hs].view(torch.int32)
+        self.starts = b8[L["starts"]:L["starts"] + 4 * hs * (n + 1)].view(torch.int32).view(hs, n + 1)
+        ntile = (n + PLAN_TILE - 1) // PLAN_TILE
+        self.plan = b8[L["plan"]:L["plan"] + 32 * heads * ntile * s].view(torch.int32).view(heads, ntile, s, 8)
+
+
+def _bins_buffer(heads, s, n, device):
+    import torch
+    nbytes = bins_layout(heads, s, n)["total"]
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def sample_bins(seed: int, sigma, s: int, n: int, device="cuda", stream=None):
+    """Draw hashes and compute their blocks on the device.  Returns
+    (delta, u, Bins) with delta/u float64 numpy [H, s]."""
+    sig = _f64(sigma).reshape(-1)
+    H = sig.size
+    delta = np.empty((H, s))
+    u = np.empty((H, s))
+    buf = _bins_buffer(H, s, n, device)
+    _check(_lib.plpsh_sample_bins(ctypes.c_uint64(seed & (2 ** 64 - 1)), H, s, n, _ptr(sig), _ptr(delta), _ptr(u),
+                                  ctypes.c_void_p(buf.data_ptr()), buf.numel(), _stream(stream)),
+           "plpsh_sample_bins")
+    return delta, u, Bins(buf, H, s, n)
+
+
+def bins_from_hashes(delta, u, n: int, device="cuda", stream=None) -> Bins:
+    d = _f64(delta)
+    uu = _f64(u)
+    H, s = d.shape
+    buf = _bins_buffer(H, s, n, device)
+    _check(_lib.plpsh_bins_from_hashes(H, s, n, _ptr(d), _ptr(uu), ctypes.c_void_p(buf.data_ptr()), buf.numel(),
+                                       _stream(stream)), "plpsh_bins_from_hashes")
+    return Bins(buf, H, s, n)
+
+
+def _qkv_shapes(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [batch, heads, n, head_dim]")
+    B, Hq, n, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != n or k.shape[3] != d:
+        raise ValueError("k and v must be [batch, heads_kv, n, head_dim] matching q")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    return B, Hq, k.shape[1], n, d
+
+
+def _workspace(workspace, heads_q, s, n, device):
+    import torch
+    need = workspace_bytes(heads_q, s, n)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace
+
+
+def attention(q, k, v, sigma, s: int, seed: int = 0, causal: bool = False, out=None, workspace=None,
+              stream=None):
+    """Positional-LSH attention (plpsh_attention_fwd)."""
+    import torch
+    B, Hq, Hkv, n, d = _qkv_shapes(q, k, v)
+    sig = _f64(sigma).reshape(-1)
+    if sig.size != Hq:
+        raise ValueError("sigma must have one entry per query head")
+    out = torch.empty_like(q) if out is None else out
+    ws = _workspace(workspace, Hq, s, n, q.device)
+    st = _lib.plpsh_attention_fwd(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                  ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()), B, Hq, Hkv, n, d,
+                                  _torch_dtype_code(q), _ptr(sig), s, ctypes.c_uint64(seed & (2 ** 64 - 1)),
+                                  int(bool(causal)), ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream))
+    _check(st, "plpsh_attention_fwd")
+    return out
+
+
+def attention_hashes(q, k, v, delta, u, causal: bool = False, out=None, workspace=None, stream=None):
+    """Positional-LSH attention with explicit hashes (plpsh_attention_fwd_hashes)."""
+    import torch
+    B, Hq, Hkv, n, d = _qkv_shapes(q, k, v)
+    dl = _f64(delta)
+    uu = _f64(u)
+    if dl.ndim != 2 or dl.shape[0] != Hq or uu.shape != dl.shape:
+        raise ValueError("delta and u must be [heads_q, s]")
+    s = dl.shape[1]
+    out = torch.empty_like(q) if out is None else out
+    ws = _workspace(workspace, Hq, s, n, q.device)
+    st = _lib.plpsh_attention_fwd_hashes(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                         ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()), B, Hq, Hkv,
+                                         n, d, _torch_dtype_code(q), _ptr(dl), _ptr(uu), s, int(bool(causal)),
+                                         ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream))
+    _check(st, "plpsh_attention_fwd_hashes")
+    return out
+
+
+def alibi_dense(q, k, v, sigma, causal: bool = False, out=None, stream=None):
+    """Exact dense ALiBi attention (plpsh_alibi_dense_fwd)."""
+    import torch
+    B, Hq, Hkv, n, d = _qkv_shapes(q, k, v)
+    sig = _f64(sigma).reshape(-1)
+    if sig.size != Hq:
+        raise ValueError("sigma must have one entry per query head")
+    out = torch.empty_like(q) if out is None else out
+    st = _lib.plpsh_alibi_dense_fwd(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                    ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()), B, Hq, Hkv, n, d,
+                                    _torch_dtype_code(q), _ptr(sig), int(bool(causal)), _stream(stream))
+    _check(st, "plpsh_alibi_dense_fwd")
+    return out

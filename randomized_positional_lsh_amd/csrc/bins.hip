@@ -1,0 +1,198 @@
+// Bin-boundary kernel: from the hashes (delta, u) to the blocks they cut the
+// positions into.
+//
+// Positional LSH (explainer of arXiv 2605.09472, Methodology 1): random
+// binning of the integer positions places x in bin floor((x - u) / delta);
+// the bins are contiguous and non-overlapping, so a hash is fully described
+// by the positions where a new block starts.  Here each hash gets one
+// workgroup that builds a bitmap of block starts in LDS, turns it into int32
+// prefix offsets (the start of every block) by a popcount scan, and writes a
+// 32-byte record per 128-row query tile for the attention kernel.
+//
+// Bit-exactness: every bin value is floor of the IEEE binary64 quotient of
+// the binary64 difference (x - u) by delta, as in the definition; this file
+// is compiled with -ffp-contract=off.  Two ways to find the starts:
+//  * delta >= 2: consecutive positions differ by at most one bin (the
+//    quotients differ by about 1/delta <= 1/2), so every bin value between
+//    bin(0) and bin(n-1) is met and block k starts at the least x whose bin
+//    is >= bin(0) + k.  That x is found from the estimate ceil(u + K delta)
+//    and corrected with exact bin evaluations (bin is non-decreasing in x).
+//  * delta < 2: evaluate every position and compare with its predecessor.
+#include <climits>
+
+#include "internal.h"
+
+namespace plpsh {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+
+__device__ __forceinline__ double bin_at(int x, double u, double delta) {
+  return floor((static_cast<double>(x) - u) / delta);
+}
+
+// Exclusive scan of one int per thread over the workgroup.
+__device__ int wg_exclusive_scan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    int t = lane < kWaves ? wsum[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < kWaves; o <<= 1) {
+      const int y = __shfl_up(t, o, 64);
+      if (lane >= o) t += y;
+    }
+    if (lane < kWaves) wsum[lane] = t;
+  }
+  __syncthreads();
+  const int base = w ? wsum[w - 1] : 0;
+  *total = wsum[kWaves - 1];
+  __syncthreads();
+  return base + x - v;
+}
+
+__global__ __launch_bounds__(kThreads) void bins_kernel(const double* __restrict__ du, int n, int s,
+                                                        int ntile, int nwords,
+                                                        int32_t* __restrict__ nblk,
+                                                        int32_t* __restrict__ starts,
+                                                        PlanRec* __restrict__ plan) {
+  extern __shared__ uint32_t lds[];
+  uint32_t* bits = lds;                                   // [nwords] start bitmap
+  int32_t* pre = reinterpret_cast<int32_t*>(lds + nwords);  // [nwords] starts before word
+  __shared__ int wsum[kWaves];
+
+  const int hid = blockIdx.x;  // hash index h * s + i
+  const int h = hid / s, i = hid - h * s;
+  const int tid = threadIdx.x;
+  const double delta = du[2 * hid], u = du[2 * hid + 1];
+
+  for (int w = tid; w < nwords; w += kThreads) bits[w] = 0u;
+  __syncthreads();
+
+  if (delta >= 2.0) {
+    const double kmin = bin_at(0, u, delta);
+    const double kmax = bin_at(n - 1, u, delta);
+    const int nb = static_cast<int>(kmax - kmin) + 1;
+    for (int k = tid + 1; k < nb; k += kThreads) {
+      const double K = kmin + static_cast<double>(k);
+      const double cand = ceil(u + K * delta);
+      int c = cand < 1.0 ? 1 : (cand > static_cast<double>(n - 1) ? n - 1 : static_cast<int>(cand));
+      // bin(c-1) < K <= bin(c); both loops move at most a step or two
+      for (int it = 0; it < 64 && c > 1 && bin_at(c - 1, u, delta) >= K; ++it) --c;
+      for (int it = 0; it < 64 && c < n - 1 && bin_at(c, u, delta) < K; ++it) ++c;
+      atomicOr(&bits[c >> 5], 1u << (c & 31));
+    }
+    if (tid == 0) atomicOr(&bits[0], 1u);
+  } else {
+    const int lane = tid & 63;
+    for (int x0 = 0; x0 < n; x0 += kThreads) {
+      const int x = x0 + tid;
+      bool f = false;
+      if (x < n) f = (x == 0) || (bin_at(x, u, delta) != bin_at(x - 1, u, delta));
+      const unsigned long long m = __ballot(f);
+      const int xw = x0 + (tid & ~63);  // multiple of 64: two whole words
+      if (lane == 0 && xw < n) {
+        bits[xw >> 5] = static_cast<uint32_t>(m);
+        bits[(xw >> 5) + 1] = static_cast<uint32_t>(m >> 32);
+      }
+    }
+  }
+  __syncthreads();
+
+  // popcount prefix over words: each thread a contiguous run of words
+  const int per = (nwords + kThreads - 1) / kThreads;
+  const int w0 = tid * per, w1 = min(w0 + per, nwords);
+  int local = 0;
+  for (int w = w0; w < w1; ++w) local += __popc(bits[w]);
+  int total;
+  int base = wg_exclusive_scan(local, wsum, &total);
+  for (int w = w0; w < w1; ++w) {
+    pre[w] = base;
+    base += __popc(bits[w]);
+  }
+  __syncthreads();
+
+  int32_t* st = starts + static_cast<size_t>(hid) * (n + 1);
+  for (int w = tid; w < nwords; w += kThreads) {
+    uint32_t m = bits[w];
+    int b = pre[w];
+    while (m) {
+      st[b++] = (w << 5) + (__ffs(m) - 1);
+      m &= m - 1;
+    }
+  }
+  if (tid == 0) {
+    nblk[hid] = total;
+    st[total] = n;
+  }
+  __threadfence_block();
+  __syncthreads();
+
+  // plan records: tile q covers rows [128 q, 128 q + 128)
+  PlanRec* pl = plan + static_cast<size_t>(h) * ntile * s + i;
+  for (int q = tid; q < ntile; q += kThreads) {
+    const int r0 = q * kPlanTile;
+    const int rl = min(r0 + kPlanTile - 1, n - 1);
+    const int x0w = r0 >> 5, xlw = rl >> 5;
+    const int kb0 = pre[x0w] + __popc(bits[x0w] & (0xFFFFFFFFu >> (31 - (r0 & 31)))) - 1;
+    const int kbl = pre[xlw] + __popc(bits[xlw] & (0xFFFFFFFFu >> (31 - (rl & 31)))) - 1;
+    PlanRec rec;
+    rec.a = st[kb0];
+    rec.e = st[kb0 + 1];
+    rec.a2 = st[kbl];
+    rec.e2 = st[kbl + 1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rec.bits[j] = bits[x0w + j];
+    rec.bits[0] &= ~1u;
+    if (n - r0 < kPlanTile) {
+      const int p = n - r0;
+      rec.bits[p >> 5] |= 1u << (p & 31);
+    }
+    pl[static_cast<size_t>(q) * s] = rec;
+  }
+}
+
+}  // namespace
+
+BinsLayout bins_layout(int heads, int s, int n) {
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  const size_t hs = static_cast<size_t>(heads) * s;
+  const size_t ntile = (static_cast<size_t>(n) + kPlanTile - 1) / kPlanTile;
+  BinsLayout L;
+  L.off_nblk = 0;
+  L.off_starts = up(hs * sizeof(int32_t));
+  L.off_plan = L.off_starts + up(hs * (static_cast<size_t>(n) + 1) * sizeof(int32_t));
+  L.total = L.off_plan + up(static_cast<size_t>(heads) * ntile * s * sizeof(PlanRec));
+  return L;
+}
+
+hipError_t launch_bins(const double* du, int heads, int s, int n, void* bins, hipStream_t stream) {
+  const BinsLayout L = bins_layout(heads, s, n);
+  char* base = static_cast<char*>(bins);
+  const int ntile = (n + kPlanTile - 1) / kPlanTile;
+  const int nwords = 4 * ntile + 4;  // covers positions < 128 (ntile + 1)
+  const size_t lds = static_cast<size_t>(nwords) * 2 * sizeof(uint32_t);
+  // opt in to the dynamic LDS this launch needs (the largest request so far)
+  static size_t attr_bytes = 0;  // benign race: the attribute only grows
+  if (lds > 64 * 1024 && lds > attr_bytes) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bins_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    attr_bytes = lds;
+  }
+  hipLaunchKernelGGL(bins_kernel, dim3(heads * s), dim3(kThreads), lds, stream, du, n, s, ntile, nwords,
+                     reinterpret_cast<int32_t*>(base + L.off_nblk),
+                     reinterpret_cast<int32_t*>(base + L.off_starts),
+                     reinterpret_cast<PlanRec*>(base + L.off_plan));
+  return hipGetLastError();
+}
+
+}  // namespace plpsh

@@ -1,0 +1,41 @@
+// Internal declarations shared by the host API and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace plpsh {
+
+// One plan record: the blocks of one hash as seen from one 128-row query
+// tile (layout documented in plpsh.h).
+struct alignas(16) PlanRec {
+  int32_t a, e;      // block containing the tile's first row
+  int32_t a2, e2;    // block containing the tile's last row
+  uint32_t bits[4];  // bit p: position r0 + p (1 <= p < 128) starts a block or equals n
+};
+static_assert(sizeof(PlanRec) == 32, "plan record is 32 bytes");
+
+constexpr int kPlanTile = 128;
+
+struct BinsLayout {
+  size_t off_nblk, off_starts, off_plan, total;
+};
+BinsLayout bins_layout(int heads, int s, int n);
+
+// Host draw (SplitMix64 counter mode, see plpsh.h).
+void draw_hashes(uint64_t seed, int heads, int s, const double* sigma, double* delta, double* u);
+
+// Device launches.  `du` points to heads*s interleaved (delta, u) pairs in
+// device-readable memory.
+hipError_t launch_bins(const double* du, int heads, int s, int n, void* bins, hipStream_t st);
+
+hipError_t launch_plsh_fwd(const void* q, const void* k, const void* v, void* o,
+                           int batch, int hq, int hkv, int n, int d, int dtype,
+                           int s, int causal, const void* bins, const uint16_t* head_order,
+                           hipStream_t st);
+
+hipError_t launch_alibi_fwd(const void* q, const void* k, const void* v, void* o,
+                            int batch, int hq, int hkv, int n, int d, int dtype,
+                            const float* beta_host, int causal, hipStream_t st);
+
+}  // namespace plpsh

@@ -1,0 +1,74 @@
+"""Shared helpers of the GPU parity tests: tolerances and oracle plumbing.
+
+Tolerances (stated for the method's outputs):
+  * float32 inputs: max |O - O_ref| <= 1e-4 elementwise.
+  * bfloat16 inputs (fp32 accumulation, P rounded to bf16 before the value
+    product): per (batch, head) slice, max |O - O_ref| / max |O_ref| <= 2e-2.
+The oracle receives the exact values the kernel read (bf16 or fp32 upcast to
+float64), so only in-kernel arithmetic is measured.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+
+TOL_F32_ABS = 1e-4
+TOL_BF16_REL = 2e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check_slices(out, ref, dtype, where=""):
+    """out, ref: float64 [..., n, d] (same shape).  Returns max errors."""
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert out.shape == ref.shape, (out.shape, ref.shape)
+    assert np.all(np.isfinite(out)), f"non-finite output {where}"
+    err = np.abs(out - ref)
+    if dtype == "f32":
+        m = err.max() if err.size else 0.0
+        assert m <= TOL_F32_ABS, f"{where}: max abs err {m:.3e} > {TOL_F32_ABS}"
+        return m
+    lead = out.shape[:-2]
+    worst = 0.0
+    for idx in np.ndindex(*lead):
+        e = err[idx].max()
+        s = np.abs(ref[idx]).max()
+        rel = e / s if s > 0 else e
+        worst = max(worst, rel)
+        assert rel <= TOL_BF16_REL, f"{where} slice {idx}: rel err {rel:.3e} > {TOL_BF16_REL}"
+    return worst
+
+
+def oracle_full(q, k, v, delta, u, causal):
+    """Full T~ with the banded oracle (identical arithmetic to the dense
+    form; pinned against it on the CPU).  q [B,Hq,n,d] float64 etc."""
+    B, Hq, n, d = q.shape
+    grp = Hq // k.shape[1]
+    out = np.empty_like(q)
+    for b in range(B):
+        for h in range(Hq):
+            o, _ = oracle.plsh_attention_rowblocks(q[b, h], k[b, h // grp], v[b, h // grp], delta[h], u[h],
+                                                   causal, row_block=64)
+            out[b, h] = o
+    return out
+
+
+def sample_rows(n, count, rng):
+    base = {0, 1, 2, n - 1, n - 2}
+    for t in (63, 64, 65, 127, 128, 129, 255, 256):
+        if t < n:
+            base.add(t)
+    extra = rng.choice(n, size=min(count, n), replace=False)
+    return np.array(sorted(base.union(int(x) for x in extra)))

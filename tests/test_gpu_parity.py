@@ -1,0 +1,283 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Bins are compared bit for bit; attention outputs within the tolerances of
+tests/_parity.py.  Small problems are compared element by element over
+every output; the full-size workloads are launched exactly as the bench
+launches them and compared on sampled rows that the oracle computes one by
+one.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests._parity import check_slices, oracle_full, sample_rows, say, to64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+P = pytest.importorskip("randomized_positional_lsh_amd")
+
+
+def _tdt(dtype):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def _qkv_dev(B, Hq, Hkv, n, d, dtype, seed, gpu, scale_q=1.0):
+    q, k, v = synth.qkv_numpy(B, Hq, Hkv, n, d, dtype, seed, scale_q)
+    t = lambda a: torch.from_numpy(a).to(gpu).to(_tdt(dtype)).contiguous()
+    return (t(q), t(k), t(v)), (q.astype(np.float64), k.astype(np.float64), v.astype(np.float64))
+
+
+# ------------------------------------------------------------------ bins --
+
+def _expected_plan(delta, u, n):
+    st = oracle.block_starts(delta, u, n)
+    ntile = (n + 127) // 128
+    rec = np.zeros((ntile, 8), dtype=np.int64)
+    starts_set = set(st.tolist()) | {n}
+    for q in range(ntile):
+        r0 = 128 * q
+        rl = min(r0 + 127, n - 1)
+        a, e = oracle.block_of(delta, u, n, [r0, rl])
+        rec[q, 0], rec[q, 1], rec[q, 2], rec[q, 3] = a[0], e[0], a[1], e[1]
+        bits = [0, 0, 0, 0]
+        for p in range(1, 128):
+            if r0 + p in starts_set:
+                bits[p >> 5] |= 1 << (p & 31)
+        rec[q, 4:] = bits
+    return st, rec
+
+
+def _check_bins(bins, delta, u, n):
+    nblk = bins.nblk.cpu().numpy()
+    starts = bins.starts.cpu().numpy()
+    plan = bins.plan.cpu().numpy().view(np.uint32).astype(np.int64)
+    H, s = delta.shape
+    for h in range(H):
+        for i in range(s):
+            t = h * s + i
+            st, rec = _expected_plan(delta[h, i], u[h, i], n)
+            assert nblk[t] == st.size, (h, i, delta[h, i], u[h, i], n)
+            assert np.array_equal(starts[t, :st.size + 1], np.append(st, n)), (h, i, delta[h, i], u[h, i], n)
+            got = plan[h, :, i, :].copy()
+            got[:, :4] = plan[h, :, i, :4].astype(np.uint32).view(np.int32)
+            assert np.array_equal(got, rec), (h, i, delta[h, i], u[h, i], n)
+
+
+@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 127, 128, 129, 1000, 4097])
+def test_bins_bit_exact_edge_widths(gpu, n):
+    widths = [0.3, 0.999, 1.0, 1.0 + 2 ** -40, 1.5, 1.999, 2.0, 2.5, 7.3, 64.0, 127.5, 1000.0, float(n), 10.0 * n, 1e9]
+    rng = np.random.default_rng(n)
+    delta, u = [], []
+    for w in widths:
+        for uu in (0.0, rng.uniform(0, w), w * (1 - 2 ** -30), w):
+            delta.append(w)
+            u.append(uu)
+    s = 4
+    delta = np.array(delta).reshape(-1, s)
+    u = np.array(u).reshape(-1, s)
+    say(f"bins edge widths n={n} hashes={delta.size}")
+    bins = P.bins_from_hashes(delta, u, n, device=gpu)
+    torch.cuda.synchronize()
+    _check_bins(bins, delta, u, n)
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "qwen3", "mistral"])
+def test_bins_bit_exact_workload_draws(gpu, name):
+    W = synth.WORKLOADS[name]
+    say(f"bins workload {name}")
+    delta, u, bins = P.sample_bins(W.hash_seed, W.sigmas, W.s, W.n, device=gpu)
+    torch.cuda.synchronize()
+    d2, u2 = oracle.sample_hashes(W.hash_seed, W.sigmas, W.s)
+    assert np.array_equal(delta, d2) and np.array_equal(u, u2)
+    heads = range(W.heads_q) if W.n <= 4096 else [0, 5, W.heads_q // 2, W.heads_q - 1]
+    nblk = bins.nblk.cpu().numpy()
+    starts = bins.starts.cpu().numpy()
+    for h in heads:
+        for i in range(W.s):
+            st = oracle.block_starts(delta[h, i], u[h, i], W.n)
+            t = h * W.s + i
+            assert nblk[t] == st.size
+            assert np.array_equal(starts[t, :st.size + 1], np.append(st, W.n))
+
+
+# ------------------------------------------------------------- attention --
+
+CASES = [
+    # B, Hq, Hkv, n, d, dtype, sigmas, s, causal
+    (1, 1, 1, 512, 64, "f32", (16.0,), 8, False),          # the tiny workload's shape
+    (1, 1, 1, 512, 64, "f32", (16.0,), 8, True),
+    (2, 4, 2, 333, 128, "f32", (1.5, 6.0, 30.0, 200.0), 6, True),
+    (2, 4, 2, 333, 128, "f32", (1.5, 6.0, 30.0, 200.0), 6, False),
+    (1, 4, 4, 1000, 64, "bf16", (1.19, 8.0, 64.0, 512.0), 20, True),
+    (1, 4, 4, 1000, 64, "bf16", (1.19, 8.0, 64.0, 512.0), 20, False),
+    (2, 6, 2, 777, 128, "bf16", (1.0, 2.0, 4.0, 16.0, 100.0, 300.0), 20, True),
+    (1, 2, 1, 777, 128, "bf16", (5.0, 80.0), 32, False),
+    (1, 2, 2, 300, 128, "bf16", (3.0, 50.0), 40, True),     # two count chunks
+    (1, 2, 2, 300, 64, "bf16", (3.0, 50.0), 100, False),    # four count chunks
+    (1, 2, 1, 1, 64, "bf16", (4.0, 8.0), 5, True),           # n = 1
+    (1, 2, 1, 65, 128, "bf16", (4.0, 8.0), 5, True),
+    (3, 2, 1, 129, 64, "f32", (0.5, 1000.0), 3, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}H{c[1]}/{c[2]}n{c[3]}d{c[4]}{c[5]}s{c[7]}{'c' if c[8] else 'nc'}")
+def test_attention_matches_oracle_small(gpu, case):
+    B, Hq, Hkv, n, d, dtype, sig, s, causal = case
+    say(f"attention small case {case}")
+    (q, k, v), (q64, k64, v64) = _qkv_dev(B, Hq, Hkv, n, d, dtype, 7 + n, gpu, scale_q=2.0)
+    delta, u = P.draw_hashes(11, sig, s)
+    o = P.attention(q, k, v, sig, s, seed=11, causal=causal)
+    torch.cuda.synchronize()
+    ref = oracle_full(q64, k64, v64, delta, u, causal)
+    err = check_slices(to64(o), ref, dtype, where=str(case))
+    say(f"  max err {err:.3e}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_workload_full_compare(gpu, name):
+    W = synth.WORKLOADS[name]
+    say(f"workload {name} full compare")
+    (q, k, v), (q64, k64, v64) = _qkv_dev(W.batch, W.heads_q, W.heads_kv, W.n, W.head_dim, W.dtype, W.data_seed, gpu)
+    o = P.attention(q, k, v, W.sigmas, W.s, seed=W.hash_seed, causal=W.causal)
+    torch.cuda.synchronize()
+    delta, u = oracle.sample_hashes(W.hash_seed, W.sigmas, W.s)
+    ref = oracle_full(q64, k64, v64, delta, u, W.causal)
+    err = check_slices(to64(o), ref, W.dtype, where=name)
+    say(f"  max err {err:.3e}")
+
+
+@pytest.mark.parametrize("name", ["qwen3", "mistral", "long"])
+def test_workload_full_size_sampled_rows(gpu, name):
+    W = synth.WORKLOADS[name]
+    say(f"workload {name} full size, sampled rows")
+    q, k, v = synth.qkv_torch(W.batch, W.heads_q, W.heads_kv, W.n, W.head_dim, W.dtype, W.data_seed, gpu)
+    ws = torch.empty(P.workspace_bytes(W.heads_q, W.s, W.n), dtype=torch.uint8, device=gpu)
+    o = torch.full_like(q, float("nan"))
+    P.attention(q, k, v, W.sigmas, W.s, seed=W.hash_seed, causal=W.causal, out=o, workspace=ws)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any().item(), "output not fully written"
+    delta, u = oracle.sample_hashes(W.hash_seed, W.sigmas, W.s)
+    rng = np.random.default_rng(5)
+    grp = W.heads_q // W.heads_kv
+    heads = range(W.heads_q) if W.n <= 16384 else range(0, W.heads_q, 3)
+    nrow = 24 if W.n <= 16384 else 10
+    worst = 0.0
+    for h in heads:
+        rows = sample_rows(W.n, nrow, rng)
+        kh = to64(k[0, h // grp])
+        vh = to64(v[0, h // grp])
+        qh = to64(q[0, h, torch.as_tensor(rows, device=gpu)])
+        ref = oracle.plsh_attention_rows(qh, kh, vh, delta[h], u[h], rows, W.causal)
+        got = to64(o[0, h, torch.as_tensor(rows, device=gpu)])
+        worst = max(worst, check_slices(got[None], ref[None], W.dtype, where=f"{name} head {h}"))
+    say(f"  worst rel err {worst:.3e}")
+
+
+def test_one_block_is_plain_attention(gpu):
+    """delta >= n, u = 0: every mask is all ones; T~ = softmax(QK^T/sqrt d) V."""
+    (q, k, v), (q64, k64, v64) = _qkv_dev(1, 2, 1, 300, 64, "bf16", 3, gpu, scale_q=3.0)
+    for causal in (False, True):
+        delta = np.full((2, 3), 300.0)
+        u = np.zeros((2, 3))
+        o = P.attention_hashes(q, k, v, delta, u, causal=causal)
+        torch.cuda.synchronize()
+        ref = oracle.plsh_attention(q64, k64, v64, delta, u, causal)
+        check_slices(to64(o), ref, "bf16", where=f"one block causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_single_position_blocks_return_v_exactly(gpu, dtype):
+    """delta < 1: each position is its own block, so T~ = V exactly.  In bf16
+    the output rounding makes it bit-exact; in fp32 the weight of the only
+    key is exp2 of a rounding residue, so the ratio is within 2 ulp."""
+    (q, k, v), _ = _qkv_dev(2, 2, 2, 257, 128, dtype, 4, gpu)
+    delta = np.array([[0.5, 0.9], [0.25, 0.999]])
+    u = delta * 0.5
+    for causal in (False, True):
+        o = P.attention_hashes(q, k, v, delta, u, causal=causal)
+        torch.cuda.synchronize()
+        if dtype == "bf16":
+            assert torch.equal(o, v), f"causal={causal}"
+        else:
+            assert torch.all((o - v).abs() <= 2 * 2.0 ** -23 * v.abs()), f"causal={causal}"
+
+
+def test_fixed_blocks(gpu):
+    """s = 1, delta = b, u = 0: deterministic partition into blocks of b."""
+    (q, k, v), (q64, k64, v64) = _qkv_dev(1, 2, 2, 500, 128, "bf16", 5, gpu)
+    delta = np.array([[16.0], [128.0]])
+    u = np.zeros((2, 1))
+    for causal in (False, True):
+        o = P.attention_hashes(q, k, v, delta, u, causal=causal)
+        torch.cuda.synchronize()
+        ref = oracle.plsh_attention(q64, k64, v64, delta, u, causal)
+        check_slices(to64(o), ref, "bf16", where=f"fixed blocks causal={causal}")
+
+
+def test_deterministic_and_canary(gpu):
+    W = synth.WORKLOADS["small"]
+    (q, k, v), _ = _qkv_dev(1, 8, 8, 1500, 64, "bf16", 6, gpu)
+    o1 = torch.full_like(q, float("nan"))
+    o2 = torch.full_like(q, float("nan"))
+    P.attention(q, k, v, W.sigmas, 10, seed=3, causal=False, out=o1)
+    P.attention(q, k, v, W.sigmas, 10, seed=3, causal=False, out=o2)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o1).any().item()
+    assert torch.equal(o1, o2)
+
+
+def test_empty_inputs(gpu):
+    q = torch.zeros((0, 2, 16, 64), dtype=torch.bfloat16, device=gpu)
+    o = P.attention(q, q[:, :1], q[:, :1], [2.0, 3.0], 4, causal=True)
+    assert o.shape == q.shape
+    q = torch.zeros((1, 2, 0, 64), dtype=torch.bfloat16, device=gpu)
+    o = P.attention(q, q[:, :1], q[:, :1], [2.0, 3.0], 4, causal=True)
+    assert o.shape == q.shape
+
+
+def test_workspace_too_small_on_device(gpu):
+    (q, k, v), _ = _qkv_dev(1, 1, 1, 128, 64, "bf16", 1, gpu)
+    ws = torch.empty(64, dtype=torch.uint8, device=gpu)
+    with pytest.raises(P.PlpshError):
+        P.attention(q, k, v, [4.0], 4, workspace=ws)
+
+
+# --------------------------------------------------------- dense ALiBi ----
+
+@pytest.mark.parametrize("case", [
+    (1, 1, 1, 512, 64, "f32", (16.0,), False),
+    (1, 1, 1, 512, 64, "f32", (16.0,), True),
+    (2, 4, 2, 333, 128, "f32", (1.5, 6.0, 30.0, 200.0), True),
+    (1, 4, 2, 1000, 128, "bf16", (1.19, 8.0, 64.0, 256.0), True),
+    (1, 4, 4, 700, 64, "bf16", (2.0, 8.0, 64.0, 1e4), False),
+])
+def test_alibi_dense_matches_oracle(gpu, case):
+    B, Hq, Hkv, n, d, dtype, sig, causal = case
+    say(f"alibi dense {case}")
+    (q, k, v), (q64, k64, v64) = _qkv_dev(B, Hq, Hkv, n, d, dtype, 9 + n, gpu, scale_q=2.0)
+    o = P.alibi_dense(q, k, v, sig, causal=causal)
+    torch.cuda.synchronize()
+    ref = oracle.alibi_attention(q64, k64, v64, sig, causal)
+    check_slices(to64(o), ref, dtype, where=f"alibi {case}")
+
+
+def test_alibi_dense_full_size_sampled(gpu):
+    W = synth.WORKLOADS["mistral"]
+    say("alibi dense mistral shape, sampled rows")
+    q, k, v = synth.qkv_torch(W.batch, W.heads_q, W.heads_kv, W.n, W.head_dim, W.dtype, W.data_seed, gpu)
+    o = P.alibi_dense(q, k, v, W.sigmas, causal=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    for h in (0, 13, 31):
+        rows = sample_rows(W.n, 8, rng)
+        kh = to64(k[0, h // 4])
+        vh = to64(v[0, h // 4])
+        qh = to64(q[0, h, torch.as_tensor(rows, device=gpu)])
+        ref = oracle.alibi_attention_rows(qh, kh, vh, W.sigmas[h], rows, True)
+        got = to64(o[0, h, torch.as_tensor(rows, device=gpu)])
+        check_slices(got[None], ref[None], "bf16", where=f"alibi mistral head {h}")
