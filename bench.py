@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Throughput of Positional-LSH ALiBi attention on one MI355X.
+
+A step is one pass of the whole path over one batch of resident inputs:
+host draw of the s hashes per head, the device bin kernel, and the fused
+attention kernel (plpsh_sample_bins + plpsh_attention_fwd_bins, i.e. what
+plpsh_attention_fwd does).  Default workload: one Mistral-7B-shaped
+attention layer (batch 1, 32 query / 8 KV heads, n = 16384, head_dim 128,
+bf16, causal, s = 20, sigma_h = 2^(8(h+1)/32)), synthetic N(0, 1) inputs.
+
+Prints ONE JSON line.  Besides the contract fields it carries:
+  roofline     : the attention kernel against the HBM roofline (algorithmic
+                 bytes = Q, K, V read once + O written once, per launch,
+                 divided by the kernel's mean duration from HIP events
+                 recorded around it on its stream)
+  cpu_baseline : the fp64 oracle timed on a bounded sample of the same
+                 workload on the host cores
+  dense_alibi  : exact ALiBi (plpsh_alibi_dense_fwd) at the same n
+  crossover    : PLSH vs dense ALiBi step times over n (Mistral shape)
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "approx-ALiBi attn tokens/s + % MFMA/HBM roofline, n=16k s=20 Mistral-7B shape"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "plsh_fwd_mistral_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "randomized_positional_lsh_amd", "csrc", "attn.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(W) -> int:
+    """Q, K, V read once and O written once (bytes per launch)."""
+    eb = 2 if W.dtype == "bf16" else 4
+    return eb * W.batch * W.n * W.head_dim * (2 * W.heads_q + 2 * W.heads_kv)
+
+
+def useful_flops(W, P, ws) -> float:
+    """4 d per (row, key) pair inside the row's support [lo(r), hi(r)) (cut
+    at r + 1 when causal), counted exactly from the block starts the bin
+    kernel wrote for this draw: the least work that yields the output."""
+    import numpy as np
+    bins = P.Bins(ws, W.heads_q, W.s, W.n)
+    nblk = bins.nblk.cpu().numpy()
+    starts = bins.starts.cpu().numpy()
+    rows = np.arange(W.n)
+    tot = 0
+    for h in range(W.heads_q):
+        lo = np.full(W.n, W.n, dtype=np.int64)
+        hi = np.zeros(W.n, dtype=np.int64)
+        for i in range(W.s):
+            t = h * W.s + i
+            st = starts[t, :nblk[t] + 1].astype(np.int64)
+            kb = np.searchsorted(st, rows, side="right") - 1
+            lo = np.minimum(lo, st[kb])
+            hi = np.maximum(hi, st[kb + 1])
+        if W.causal:
+            hi = np.minimum(hi, rows + 1)
+        tot += int((hi - lo).sum())
+    return 4.0 * W.head_dim * W.batch * tot
+
+
+class Runner:
+    """One step of the whole path with pre-marshalled C arguments."""
+
+    def __init__(self, P, W, q, k, v, o, dev):
+        import numpy as np
+        import torch
+        self.P, self.W = P, W
+        self.lib = P.raw()
+        self.sig = np.ascontiguousarray(W.sigmas, dtype=np.float64)
+        self.delta = np.empty(W.heads_q * W.s)
+        self.u = np.empty(W.heads_q * W.s)
+        nb = P.bins_layout(W.heads_q, W.s, W.n)["total"]
+        self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        self.q, self.k, self.v, self.o = q, k, v, o
+        self.dtype = 1 if W.dtype == "bf16" else 0
+        dp = ctypes.POINTER(ctypes.c_double)
+        self.p_sig = self.sig.ctypes.data_as(dp)
+        self.p_delta = self.delta.ctypes.data_as(dp)
+        self.p_u = self.u.ctypes.data_as(dp)
+        self.vp = [ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, o)]
+        self.p_ws = ctypes.c_void_p(self.ws.data_ptr())
+        self.nws = self.ws.numel()
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def bins(self):
+        W = self.W
+        st = self.lib.plpsh_sample_bins(W.hash_seed, W.heads_q, W.s, W.n, self.p_sig, self.p_delta, self.p_u,
+                                        self.p_ws, self.nws, self.stream)
+        if st:
+            raise RuntimeError(self.P.status_string(st))
+
+    def attn(self):
+        W = self.W
+        st = self.lib.plpsh_attention_fwd_bins(*self.vp, W.batch, W.heads_q, W.heads_kv, W.n, W.head_dim, self.dtype,
+                                               W.s, int(W.causal), self.p_ws, self.nws, self.p_delta, self.stream)
+        if st:
+            raise RuntimeError(self.P.status_string(st))
+
+
+def time_steps(run, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        run.bins()
+        run.attn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        run.bins()
+        a.record()
+        run.attn()
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = [a.elapsed_time(b) for a, b in ev]  # ms
+    return wall, kern
+
+
+def cpu_baseline(W, q, k, v, delta, u, seconds):
+    """The oracle, as it stands, on a bounded sample of the workload: 64-row
+    blocks taken round-robin over all heads (so every sigma is represented)
+    until `seconds` of wall time have passed."""
+    import numpy as np
+    import oracle
+    try:
+        import threadpoolctl
+        cores = sum(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()
+                    if i.get("user_api") == "blas") or 1
+    except Exception:
+        cores = 1
+    rng = np.random.default_rng(0)
+    nblk = (W.n + 63) // 64
+    order = rng.permutation(nblk)
+    grp = W.heads_q // W.heads_kv
+    kh = [k[0, g].float().cpu().numpy().astype(np.float64) for g in range(W.heads_kv)]
+    vh = [v[0, g].float().cpu().numpy().astype(np.float64) for g in range(W.heads_kv)]
+    qh = [q[0, h].float().cpu().numpy().astype(np.float64) for h in range(W.heads_q)]
+    rows = 0
+    tasks = 0
+    t0 = time.perf_counter()
+    for blk in order:
+        for h in range(W.heads_q):
+            out, rr = oracle.plsh_attention_rowblocks(qh[h], kh[h // grp], vh[h // grp], delta[h], u[h], W.causal,
+                                                      row_block=64, blocks=[int(blk)])
+            rows += out.shape[0]
+            tasks += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    rows_per_s = rows / el
+    return {
+        "value": rows_per_s / W.heads_q,  # a token needs one output row in every head
+        "unit": "tokens/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{tasks} (head, 64-row block) tasks = {rows} output rows over all {W.heads_q} heads "
+                  f"in {el:.1f} s (banded fp64 oracle, hash seed {W.hash_seed})",
+    }
+
+
+def dense_alibi(P, W, q, k, v, steps=10, warmup=3):
+    import torch
+    o = torch.empty_like(q)
+    for _ in range(warmup):
+        P.alibi_dense(q, k, v, W.sigmas, causal=W.causal, out=o)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        P.alibi_dense(q, k, v, W.sigmas, causal=W.causal, out=o)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def crossover(P, synth, dev, ns, steps=5):
+    import torch
+    out = {"n": [], "plsh_ms": [], "dense_ms": []}
+    for n in ns:
+        W = synth.Workload(f"mistral-n{n}", 1, 32, 8, n, 128, "bf16", synth.alibi_sigmas(32), 20, True, 0, 1003)
+        q, k, v = synth.qkv_torch(1, 32, 8, n, 128, "bf16", 1003, dev)
+        run = Runner(P, W, q, k, v, torch.empty_like(q), dev)
+        wall, _ = time_steps(run, steps, 2)
+        dms = dense_alibi(P, W, q, k, v, steps=steps, warmup=2)
+        out["n"].append(n)
+        out["plsh_ms"].append(round(1e3 * wall / steps, 4))
+        out["dense_ms"].append(round(dms, 4))
+        del q, k, v, run
+        torch.cuda.empty_cache()
+    cross = None
+    for n, a, b in zip(out["n"], out["plsh_ms"], out["dense_ms"]):
+        if a < b:
+            cross = n
+            break
+    out["crossover_n"] = cross
+    return out
+
+
+def copy_calibration(dev, nbytes=1 << 30, reps=5):
+    """A plain device copy of known size, for scaling HBM counters."""
+    import torch
+    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).normal_()
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} copies of {nbytes} bytes")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="mistral")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-crossover", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true", help="only run a 1 GiB device copy (counter scaling)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        log(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): the Positional-LSH path here "
+            "is single-GPU; multi-GPU sharding is a design note, not built.")
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import randomized_positional_lsh_amd as P
+    import synth
+
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(dev)
+        return
+
+    W = synth.WORKLOADS[args.workload]
+    log(f"workload {W.name}: B={W.batch} Hq={W.heads_q} Hkv={W.heads_kv} n={W.n} d={W.head_dim} {W.dtype} "
+        f"s={W.s} causal={W.causal}")
+    q, k, v = synth.qkv_torch(W.batch, W.heads_q, W.heads_kv, W.n, W.head_dim, W.dtype, W.data_seed, dev)
+    o = torch.empty_like(q)
+    run = Runner(P, W, q, k, v, o, dev)
+    wall, kern = time_steps(run, args.steps, args.warmup)
+    ms_step = 1e3 * wall / args.steps
+    tokens = W.batch * W.n
+    value = tokens / (wall / args.steps)
+    kern_ms = float(np.mean(kern))
+    log(f"step {ms_step:.4f} ms, attention kernel {kern_ms:.4f} ms (p10 {np.percentile(kern, 10):.4f}, "
+        f"p90 {np.percentile(kern, 90):.4f})")
+
+    delta = run.delta.reshape(W.heads_q, W.s).copy()
+    u = run.u.reshape(W.heads_q, W.s).copy()
+    abytes = algorithmic_bytes(W)
+    achieved = abytes / (kern_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_sha") == kernel_sha() and tr.get("workload") == W.name:
+            traffic = int(tr["bytes_per_launch"])
+    flops = useful_flops(W, P, run.ws)
+    tflops = flops / (kern_ms * 1e-3) / 1e12
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "plpsh fwd_kernel (attention)", "kernel_ms": round(kern_ms, 5),
+                "algorithmic_bytes": abytes,
+                "useful_tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": W.dtype, "data": "synthetic N(0,1) Q/K/V, hash seed 0",
+        "config": {"workload": f"{W.name}-layer", "batch": W.batch, "heads_q": W.heads_q, "heads_kv": W.heads_kv,
+                   "n": W.n, "head_dim": W.head_dim, "s": W.s, "causal": W.causal,
+                   "sigma": "2^(8(h+1)/H)", "parallelism": "single GPU"},
+        "roofline": roofline,
+    }
+    if not args.no_dense:
+        dms = dense_alibi(P, W, q, k, v)
+        line["dense_alibi"] = {"ms": round(dms, 4), "tokens_per_s": round(tokens / (dms * 1e-3), 1),
+                               "speedup_plsh_vs_dense": round(dms / ms_step, 2)}
+        log(f"dense exact ALiBi {dms:.4f} ms")
+    if not args.no_crossover and W.name == "mistral":
+        del o
+        line["crossover"] = crossover(P, synth, dev, [512, 1024, 2048, 4096, 8192, 16384, 32768, 65536])
+        log(f"crossover {line['crossover']}")
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(W, q, k, v, delta, u, args.cpu_seconds)
+        log(f"cpu baseline {line['cpu_baseline']}")
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

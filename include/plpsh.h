@@ -208,6 +208,25 @@ plpsh_status plpsh_attention_fwd_hashes(const void* q, const void* k, const void
                                         void* stream);
 
 /*
+ * plpsh_attention_fwd_bins -- the attention step alone, on a bin buffer
+ * already computed by plpsh_sample_bins / plpsh_bins_from_hashes for the
+ * same (heads_q, s, n).  plpsh_attention_fwd is exactly plpsh_sample_bins
+ * followed by this call; splitting them lets one draw serve several calls.
+ *
+ *   bins   : device, >= plpsh_bins_bytes(heads_q, s, n) bytes, 256-byte
+ *            aligned, written by the bin kernel for these sizes (the
+ *            library cannot check its contents).
+ *   delta  : host [heads_q * s] or NULL.  Only used to schedule heads with
+ *            the widest bins first; NULL keeps the natural head order.
+ * Other arguments, layouts and errors as plpsh_attention_fwd.
+ */
+plpsh_status plpsh_attention_fwd_bins(const void* q, const void* k, const void* v, void* o,
+                                      int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                      int32_t n, int32_t head_dim, plpsh_dtype dtype,
+                                      int32_t s, int32_t causal, const void* bins,
+                                      size_t bins_bytes, const double* delta, void* stream);
+
+/*
  * plpsh_alibi_dense_fwd -- exact ALiBi attention T* (the quantity the
  * approximation targets, Methodology 1), dense over all keys:
  *   O_r = sum_j C[r,j] exp(S[r,j] - |r-j|/sigma_h) v_j / sum_j (same weights)

@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     PlpshError,
     alibi_dense,
     attention,
+    attention_from_bins,
     attention_hashes,
     bins_from_hashes,
     bins_layout,

@@ -54,6 +54,8 @@ _SIGS = {
                                      _dp, _c_int, ctypes.c_uint64, _c_int, _vp, _c_sz, _vp]),
     "plpsh_attention_fwd_hashes": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                             _dp, _dp, _c_int, _c_int, _vp, _c_sz, _vp]),
+    "plpsh_attention_fwd_bins": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                          _c_int, _c_int, _vp, _c_sz, _dp, _vp]),
     "plpsh_alibi_dense_fwd": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _dp, _c_int, _vp]),
 }
@@ -157,14 +159,16 @@ def _bins_buffer(heads, s, n, device):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def sample_bins(seed: int, sigma, s: int, n: int, device="cuda", stream=None):
+def sample_bins(seed: int, sigma, s: int, n: int, device="cuda", stream=None, buffer=None, delta=None, u=None):
     """Draw hashes and compute their blocks on the device.  Returns
-    (delta, u, Bins) with delta/u float64 numpy [H, s]."""
+    (delta, u, Bins) with delta/u float64 numpy [H, s].  ``buffer`` (device
+    uint8 tensor) and ``delta``/``u`` (float64 [H, s]) may be supplied to
+    reuse storage."""
     sig = _f64(sigma).reshape(-1)
     H = sig.size
-    delta = np.empty((H, s))
-    u = np.empty((H, s))
-    buf = _bins_buffer(H, s, n, device)
+    delta = np.empty((H, s)) if delta is None else delta
+    u = np.empty((H, s)) if u is None else u
+    buf = _bins_buffer(H, s, n, device) if buffer is None else buffer
     _check(_lib.plpsh_sample_bins(ctypes.c_uint64(seed & (2 ** 64 - 1)), H, s, n, _ptr(sig), _ptr(delta), _ptr(u),
                                   ctypes.c_void_p(buf.data_ptr()), buf.numel(), _stream(stream)),
            "plpsh_sample_bins")
@@ -236,6 +240,23 @@ def attention_hashes(q, k, v, delta, u, causal: bool = False, out=None, workspac
                                          n, d, _torch_dtype_code(q), _ptr(dl), _ptr(uu), s, int(bool(causal)),
                                          ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream))
     _check(st, "plpsh_attention_fwd_hashes")
+    return out
+
+
+def attention_from_bins(q, k, v, bins: "Bins", causal: bool = False, delta=None, out=None, stream=None):
+    """The attention step on a computed bin buffer (plpsh_attention_fwd_bins)."""
+    import torch
+    B, Hq, Hkv, n, d = _qkv_shapes(q, k, v)
+    if bins.heads != Hq or bins.n != n:
+        raise ValueError("bins were computed for other sizes")
+    dl = None if delta is None else _f64(delta)
+    out = torch.empty_like(q) if out is None else out
+    st = _lib.plpsh_attention_fwd_bins(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                       ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()), B, Hq, Hkv, n,
+                                       d, _torch_dtype_code(q), bins.s, int(bool(causal)),
+                                       ctypes.c_void_p(bins.buffer.data_ptr()), bins.buffer.numel(),
+                                       None if dl is None else _ptr(dl), _stream(stream))
+    _check(st, "plpsh_attention_fwd_bins")
     return out
 
 

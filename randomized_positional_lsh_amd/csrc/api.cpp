@@ -129,25 +129,33 @@ plpsh_status check_qkv(const void* q, const void* k, const void* v, void* o, int
   return PLPSH_OK;
 }
 
+// Launch the attention kernel on a computed bin buffer.  Heads with the
+// widest bins (largest key windows) are scheduled first when delta is known.
+plpsh_status attention_on_bins(const void* q, const void* k, const void* v, void* o, int batch, int hq, int hkv,
+                               int n, int d, int dtype, const double* delta, int s, int causal, const void* bins,
+                               hipStream_t st) {
+  std::vector<uint16_t> order(hq);
+  std::iota(order.begin(), order.end(), 0);
+  if (delta) {
+    std::vector<double> cost(hq, 0.0);
+    for (int h = 0; h < hq; ++h)
+      for (int i = 0; i < s; ++i) cost[h] += std::min(delta[h * s + i], static_cast<double>(n));
+    std::stable_sort(order.begin(), order.end(), [&](uint16_t a, uint16_t b) { return cost[a] > cost[b]; });
+  }
+  if (hip_failed(plpsh::launch_plsh_fwd(q, k, v, o, batch, hq, hkv, n, d, dtype, s, causal, bins, order.data(), st),
+                 "attention kernel launch"))
+    return PLPSH_ERR_HIP;
+  return PLPSH_OK;
+}
+
 plpsh_status attention_common(const void* q, const void* k, const void* v, void* o, int batch, int hq, int hkv,
                               int n, int d, int dtype, const double* delta, const double* u, int s, int causal,
-                              void* ws, size_t ws_bytes, void* stream) {
+                              void* ws, void* stream) {
   if (batch == 0 || n == 0) return PLPSH_OK;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   plpsh_status r = run_bins(hq, s, n, delta, u, ws, st);
   if (r != PLPSH_OK) return r;
-  // heads with the widest bins first (largest key windows)
-  std::vector<double> cost(hq, 0.0);
-  for (int h = 0; h < hq; ++h)
-    for (int i = 0; i < s; ++i) cost[h] += std::min(delta[h * s + i], static_cast<double>(n));
-  std::vector<uint16_t> order(hq);
-  std::iota(order.begin(), order.end(), 0);
-  std::stable_sort(order.begin(), order.end(), [&](uint16_t a, uint16_t b) { return cost[a] > cost[b]; });
-  if (hip_failed(plpsh::launch_plsh_fwd(q, k, v, o, batch, hq, hkv, n, d, dtype, s, causal, ws, order.data(), st),
-                 "attention kernel launch"))
-    return PLPSH_ERR_HIP;
-  (void)ws_bytes;
-  return PLPSH_OK;
+  return attention_on_bins(q, k, v, o, batch, hq, hkv, n, d, dtype, delta, s, causal, ws, st);
 }
 
 }  // namespace
@@ -238,7 +246,7 @@ plpsh_status plpsh_attention_fwd(const void* q, const void* k, const void* v, vo
   std::vector<double> dl(hs), uu(hs);
   plpsh::draw_hashes(seed, heads_q, s, sigma, dl.data(), uu.data());
   return attention_common(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, dl.data(), uu.data(), s,
-                          causal, workspace, workspace_bytes, stream);
+                          causal, workspace, stream);
 }
 
 plpsh_status plpsh_attention_fwd_hashes(const void* q, const void* k, const void* v, void* o, int32_t batch,
@@ -252,7 +260,25 @@ plpsh_status plpsh_attention_fwd_hashes(const void* q, const void* k, const void
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255)) return PLPSH_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < plpsh_workspace_bytes(heads_q, s, n)) return PLPSH_ERR_WORKSPACE_TOO_SMALL;
   return attention_common(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, delta, u, s, causal,
-                          workspace, workspace_bytes, stream);
+                          workspace, stream);
+}
+
+plpsh_status plpsh_attention_fwd_bins(const void* q, const void* k, const void* v, void* o, int32_t batch,
+                                      int32_t heads_q, int32_t heads_kv, int32_t n, int32_t head_dim,
+                                      plpsh_dtype dtype, int32_t s, int32_t causal, const void* bins,
+                                      size_t bins_bytes, const double* delta, void* stream) {
+  plpsh_status r = check_qkv(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, causal);
+  if (r != PLPSH_OK) return r;
+  if (!valid_hs(heads_q, s)) return PLPSH_ERR_INVALID_ARGUMENT;
+  if (batch == 0 || n == 0) return PLPSH_OK;
+  if (!bins || (reinterpret_cast<uintptr_t>(bins) & 255)) return PLPSH_ERR_INVALID_ARGUMENT;
+  if (bins_bytes < plpsh::bins_layout(heads_q, s, n).total) return PLPSH_ERR_WORKSPACE_TOO_SMALL;
+  if (delta) {
+    for (long long i = 0; i < static_cast<long long>(heads_q) * s; ++i)
+      if (!finite_pos(delta[i])) return PLPSH_ERR_INVALID_ARGUMENT;
+  }
+  return attention_on_bins(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, delta, s, causal, bins,
+                           static_cast<hipStream_t>(stream));
 }
 
 plpsh_status plpsh_alibi_dense_fwd(const void* q, const void* k, const void* v, void* o, int32_t batch,
