@@ -7,37 +7,44 @@
 //   O_r = sum_j c[r,j] C[r,j] e^{S[r,j]} v_j / sum_j c[r,j] C[r,j] e^{S[r,j]},
 //   c[r,j] = #{i : bin_i(r) == bin_i(j)},  S = Q K^T / sqrt(d).
 //
-// All s hashes share one pass over the keys: the logits and the exponentials
-// are computed once per (query, key) pair and weighted by the integer count
-// c, which is itself produced by the matrix cores in the layout of S.
+// All s hashes share one pass over the keys: the logits and exponentials are
+// computed once per (query, key) pair and weighted by the integer count c,
+// which the matrix cores produce in the layout of S.
 //
 // Work decomposition.  One workgroup (4 waves) owns 128 query rows of one
 // (batch, head); wave w owns rows 32w..32w+31 as two 16-row blocks.  Keys
-// are streamed in 64-key tiles through LDS (double buffered): first the two
-// "near" tiles covering the query rows themselves, then the tiles to the
-// left down to the smallest block start of the tile's first row, then (when
-// not causal) the tiles to the right up to the largest block end of its last
-// row.  Nothing outside that window can have c > 0.
+// stream through LDS in 64-key tiles, two stages deep, loaded straight from
+// HBM into LDS by buffer loads (rows past the sequence end read as zero).
+// Order: the two "near" tiles holding the query rows themselves, then tiles
+// to the left down to the smallest block start of the first row, then (not
+// causal) tiles to the right up to the largest block end of the last row;
+// nothing outside that window has c > 0.
 //
-// Counts as a matrix product (exact small integers in bf16, fp32 result):
-//  * keys left of the tile (j < r0): hash i contributes to (r, j) iff its
-//    block [a_i, e_i) containing r0 also contains r and j, i.e.
-//    [r < e_i] [j >= a_i].  So c = U V^T over a K dimension of one slot per
-//    hash, with U[r,i] = [r < e_i] (fixed per query tile) and
-//    V[j,i] = [j >= a_i], a prefix of ones once the hashes are sorted by a_i.
-//  * keys right of the tile: symmetric with the block containing the last row.
-//  * keys among the tile's own rows: c[r,j] = sum_{p <= j} H[r,p] where
-//    H[r,p] counts hashes whose block of r starts at p (clamped to r0) minus
-//    those whose block of r ends at p; the sum over p <= j is a product with
-//    the constant lower-triangular matrix [p <= j] (K = 128 positions).
+// LDS layouts.  K and V tiles are row-major (one key per row) with their
+// 16-byte chunks XOR-swizzled by key so that the logit operand reads (one
+// 16-byte chunk per lane) and the transposing value-operand reads
+// (ds_read_b64_tr_b16: lane 4a+b of each 16-lane group receives element b
+// of lanes a, a+4, a+8, a+12) are free of bank conflicts.
 //
-// Softmax: running row maximum shared by all hashes, rescaled only when a
-// tile's maximum exceeds it by more than 2^8 in the exponential (so the
-// rescale is rare); masked entries (c = 0, or j > r when causal) enter as
-// -inf; the first tile processed contains the diagonal, where c = s > 0.
+// Counts as matrix products (exact small integers in bf16, fp32 result):
+//  * keys left of the tile (j < r0): hash i adds 1 to (r, j) iff its block
+//    [a_i, e_i) containing r0 also contains r and j, i.e. [r < e_i][j >= a_i].
+//    So c = U V^T with one K-slot per hash: U[r,i] = [r < e_i] is fixed per
+//    query tile and V[j,i] = [j >= a_i] is a prefix of ones once the hashes
+//    are sorted by a_i (taken from a 9-entry table of bf16 prefixes).
+//  * keys right of the tile: the same with the block containing the last row.
+//  * keys among the tile's own rows: c[r,j] = sum_{p <= j} H[r,p] where H
+//    counts hashes whose block of r starts at position p (clamped to r0)
+//    minus those whose block of r ends at p; summing over p <= j is a
+//    product with the constant matrix [p <= j] (K = 128 positions).
 //
-// The dense exact-ALiBi variant (MODE_ALIBI) uses the same skeleton with the
-// weight e^{S - |r-j|/sigma} over every key.
+// Softmax: one running row maximum shared by all hashes.  It is raised only
+// when a tile exceeds it by more than 2^8 in the exponential, so rescaling
+// is rare; masked entries (c = 0, or j > r when causal) enter as -inf; the
+// first tile holds the diagonal, where c = s > 0.
+//
+// MODE_ALIBI computes exact dense ALiBi attention, weight e^{S - |r-j|/sigma},
+// over every key with the same pipeline.
 #include <climits>
 #include <type_traits>
 
@@ -47,14 +54,20 @@ namespace plpsh {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-constexpr int NT = 256;   // threads per workgroup
-constexpr int BM = 128;   // query rows per workgroup
-constexpr int BN = 64;    // keys per tile
-constexpr int MAXS = 128; // hashes per head
+constexpr int NT = 256;    // threads per workgroup
+constexpr int NW = 4;      // waves per workgroup
+constexpr int BM = 128;    // query rows per workgroup
+constexpr int BN = 64;     // keys per tile
+constexpr int MAXS = 128;  // hashes per head
 constexpr float kLog2e = 1.4426950408889634f;
 
 enum { MODE_PLSH = 0, MODE_ALIBI = 1 };
@@ -69,45 +82,44 @@ struct FwdArgs {
   int B, Hq, Hkv, n, s, ntile, cs;
 };
 
-template <int D, bool BF, int MODE>
-struct Cfg {
+template <int D, bool BF>
+struct Geo {
   using T = typename std::conditional<BF, uint16_t, float>::type;
-  static constexpr int EPC = 16 / sizeof(T);           // elements per 16-byte chunk
-  static constexpr int CPR = D / EPC;                  // chunks per key row
-  static constexpr int KSTR = D + EPC;                 // K row stride (elements), +16 bytes
-  static constexpr int VSTR = BN + 4;                  // transposed V row stride (keys)
-  static constexpr int K_ELEMS = BN * KSTR;
-  static constexpr int V_ELEMS = D * VSTR;
-  static constexpr int KV_BYTES = 2 * (K_ELEMS + V_ELEMS) * static_cast<int>(sizeof(T));
-  static constexpr int HSTR = BM + 8;                  // H row stride (bf16)
-  static constexpr int H_BYTES = MODE == MODE_PLSH ? BM * HSTR * 2 : 0;
-  static constexpr int BIG = ((KV_BYTES > H_BYTES ? KV_BYTES : H_BYTES) + 15) / 16 * 16;
-  static constexpr int SMALL = MODE == MODE_PLSH ? MAXS * 32 + 4 * MAXS * 4 + 9 * 16 + 64 : 64;
-  static constexpr int LDS = BIG + SMALL;
-  static constexpr int KLD = BN * CPR / NT;            // 16-byte K loads per thread
-  static constexpr int UNITS = (BN / 4) * CPR;         // 4-key x 16-byte V units
-  static constexpr int VIT = (UNITS + NT - 1) / NT;    // V units per thread
-  static constexpr int KS = BF ? D / 32 : D / 4;       // k-steps of the logit product
-  static constexpr int DB = D / 16;                    // 16-wide output column blocks
+  static constexpr int ES = sizeof(T);
+  static constexpr int RB = D * ES;                  // bytes per key row
+  static constexpr int CPR = RB / 16;                // 16-byte chunks per row
+  static constexpr int RPI = 1024 / RB;              // rows per 1 KB load instruction
+  static constexpr int TILE = BN * RB;               // bytes of one K or V tile
+  static constexpr int NI = TILE / 1024 / NW;        // load instructions per wave per matrix
+  static constexpr int STAGE = 2 * TILE;             // K tile + V tile
+  static constexpr int HC = BM * BM * 2;             // near counts, bf16 [p][r]
+  static constexpr int BIG = 2 * STAGE > STAGE + HC ? 2 * STAGE : STAGE + HC;
+  static constexpr int KS = BF ? D / 32 : D / 4;     // k-steps of the logit product
+  static constexpr int DB = D / 16;                  // 16-wide output column blocks
+  __device__ static int swk(int key) { return key & 15 & (CPR - 1); }
+  __device__ static int swv(int key) { return CPR >= 16 ? 2 * (key & 7) : 2 * (key & 3); }
 };
 
+// small-LDS region: plan records, sorted hash arrays, prefix table, scalars
+constexpr int SM_REC = 0;
+constexpr int SM_AA = SM_REC + MAXS * 32;  // a_i sorted ascending
+constexpr int SM_AE = SM_AA + MAXS * 4;    // e_i in that order
+constexpr int SM_EE = SM_AE + MAXS * 4;    // e2_i sorted descending
+constexpr int SM_EA = SM_EE + MAXS * 4;    // a2_i in that order
+constexpr int SM_TH = SM_EA + MAXS * 4;    // 9 x 16-byte bf16 prefixes of ones
+constexpr int SM_SC = SM_TH + 9 * 16;      // scalars
+constexpr int SMALL = SM_SC + 64;
+
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  const __bf16 a = static_cast<__bf16>(lo), b = static_cast<__bf16>(hi);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
-}
-__device__ __forceinline__ float bf16_bits_to_f32(uint16_t x) {
-  return __uint_as_float(static_cast<uint32_t>(x) << 16);
-}
-__device__ __forceinline__ uint16_t f32_to_bf16_exact(float x) {  // x is a small integer
-  return static_cast<uint16_t>(__float_as_uint(x) >> 16);
+  const f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 __device__ __forceinline__ float xmax16(float x) {  // max over the 4 lanes sharing lane & 15
   x = fmaxf(x, __shfl_xor(x, 16, 64));
@@ -117,98 +129,284 @@ __device__ __forceinline__ float xsum16(float x) {
   x += __shfl_xor(x, 16, 64);
   return x + __shfl_xor(x, 32, 64);
 }
-__device__ __forceinline__ int clamp08(int x) { return x < 0 ? 0 : (x > 8 ? 8 : x); }
+__device__ __forceinline__ int clamp08(int x) { return min(max(x, 0), 8); }
+__device__ __forceinline__ u32x4 lds128(const unsigned char* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x2 lds_tr16(const unsigned char* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(const_cast<unsigned char*>(p)));
+  return __builtin_bit_cast(u32x2, v);
+}
 
-template <int D, bool BF, int MODE>
-struct Tile {
-  using C = Cfg<D, BF, MODE>;
-  using T = typename C::T;
-  u32x4 k[C::KLD];
-  u32x4 v[C::VIT][4];
+template <int D, bool BF>
+struct TileLoader {
+  using G = Geo<D, BF>;
+  int koff[G::NI], voff[G::NI];  // per-lane byte offsets inside a tile (constant)
 
-  __device__ __forceinline__ void load(const T* __restrict__ Kp, const T* __restrict__ Vp, int j0, int n,
-                                       int tid) {
+  __device__ __forceinline__ void init(int w, int lane) {
 #pragma unroll
-    for (int it = 0; it < C::KLD; ++it) {
-      const int idx = tid + NT * it;
-      const int key = idx / C::CPR, ch = idx % C::CPR;
-      const int j = j0 + key;
-      k[it] = (j >= 0 && j < n) ? *reinterpret_cast<const u32x4*>(Kp + static_cast<size_t>(j) * D + ch * C::EPC)
-                                : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < G::NI; ++i) {
+      const int I = w * G::NI + i;
+      const int key = I * G::RPI + lane / G::CPR;
+      const int pc = lane % G::CPR;
+      koff[i] = key * G::RB + 16 * (pc ^ G::swk(key));
+      voff[i] = key * G::RB + 16 * (pc ^ G::swv(key));
     }
+  }
+  // K/V rows j0 .. j0 + 63 into one stage; rows at or past n read as zero.
+  __device__ __forceinline__ void issue(const void* Kh, const void* Vh, int j0, int n, unsigned char* stage,
+                                        int w) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    // (the host compilation pass must not see this builtin: with it, clang
+    // silently omits the host launch stubs of the kernels that inline it)
+    const int rows = n - j0;
+    const int nrec = rows > 0 ? rows * G::RB : 0;
+    const size_t off = static_cast<size_t>(j0) * G::RB;
+    __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(static_cast<const char*>(Kh)) + off, (short)0, nrec, 0x00020000);
+    __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(static_cast<const char*>(Vh)) + off, (short)0, nrec, 0x00020000);
 #pragma unroll
-    for (int it = 0; it < C::VIT; ++it) {
-      const int u = tid + NT * it;
-      const int ch = u % C::CPR, kq = u / C::CPR;
+    for (int i = 0; i < G::NI; ++i) {
+      const int I = w * G::NI + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(stage + I * 1024), 16, koff[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(stage + G::TILE + I * 1024), 16, voff[i], 0, 0, 0);
+    }
+#endif
+  }
+};
+
+template <int D, bool BF, bool CAUSAL, int NCH, int MODE>
+struct Fwd {
+  using G = Geo<D, BF>;
+  using T = typename G::T;
+  static constexpr bool PL = MODE == MODE_PLSH;
+  static constexpr int KS = G::KS, DB = G::DB;
+
+  // per-lane state
+  int lane, l16, g, w;
+  int rr[2], R[2];
+  float sc, scp, thr, beta;
+  float Mrow[2], Msc[2], lsum[2];
+  f32x4 acc[DB][2];
+  u32x4 qb[2][BF ? KS : 1];
+  float qf[2][BF ? 1 : KS];
+  int koff[BF ? KS : KS / 4];  // logit-operand chunk offsets within a row block
+  int vtr[DB];                 // value-operand (transposing read) offsets
+  const unsigned char* sTh;
+
+  __device__ __forceinline__ void init_offsets() {
+    // K operand: key = 16 kb + l16; logical chunk c = 4 ks + g (bf16) or (KS/4) g + c4 (fp32)
+    if constexpr (BF) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int j = j0 + 4 * kq + t;
-        v[it][t] = (u < C::UNITS && j >= 0 && j < n)
-                       ? *reinterpret_cast<const u32x4*>(Vp + static_cast<size_t>(j) * D + ch * C::EPC)
-                       : u32x4{0, 0, 0, 0};
-      }
+      for (int ks = 0; ks < KS; ++ks) koff[ks] = l16 * G::RB + 16 * ((4 * ks + g) ^ G::swk(l16));
+    } else {
+#pragma unroll
+      for (int c4 = 0; c4 < KS / 4; ++c4) koff[c4] = l16 * G::RB + 16 * (((KS / 4) * g + c4) ^ G::swk(l16));
+    }
+    // V operand
+    if constexpr (BF) {
+      const int a = l16 & 3, t = l16 >> 2;
+      const int key = 4 * g + t;  // + 32 kc + 16 hh: multiples of 8, swizzle unchanged
+#pragma unroll
+      for (int db = 0; db < DB; ++db) vtr[db] = key * G::RB + 16 * ((2 * db + (a >> 1)) ^ G::swv(key)) + 8 * (a & 1);
+    } else {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) vtr[db] = 0;
     }
   }
 
-  // K row-major [key][dim]; V transposed [dim][key].
-  __device__ __forceinline__ void store(T* __restrict__ sK, T* __restrict__ sV, int tid) const {
+  // ---- one 32-key chunk of a tile: logits, counts, softmax, value product
+  template <int KIND>
+  __device__ __forceinline__ void chunk(const unsigned char* sK, const unsigned char* sV, int j0, int r0, int n,
+                                        int kc, bool need_mask, const int (&mkey)[4], const u32x4 (&cnt_b)[2][4],
+                                        int chmax) {
+    const int jc = j0 + 32 * kc;
+    f32x4 sacc[2][2], cacc[2][2];
 #pragma unroll
-    for (int it = 0; it < C::KLD; ++it) {
-      const int idx = tid + NT * it;
-      const int key = idx / C::CPR, ch = idx % C::CPR;
-      *reinterpret_cast<u32x4*>(sK + key * C::KSTR + ch * C::EPC) = k[it];
-    }
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int it = 0; it < C::VIT; ++it) {
-      const int u = tid + NT * it;
-      if (u >= C::UNITS) continue;
-      const int ch = u % C::CPR, kq = u / C::CPR;
+      for (int rb = 0; rb < 2; ++rb) {
+        sacc[x][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        cacc[x][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    // S^T = K Q^T
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      const unsigned char* kr = sK + (16 * (2 * kc + kb2)) * G::RB;
       if constexpr (BF) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint32_t r0 = v[it][0][m], r1 = v[it][1][m], r2 = v[it][2][m], r3 = v[it][3][m];
-          const u32x2 lo = {(r0 & 0xFFFFu) | (r1 << 16), (r2 & 0xFFFFu) | (r3 << 16)};
-          const u32x2 hi = {(r0 >> 16) | (r1 & 0xFFFF0000u), (r2 >> 16) | (r3 & 0xFFFF0000u)};
-          const int dim = ch * 8 + 2 * m;
-          *reinterpret_cast<u32x2*>(sV + dim * C::VSTR + 4 * kq) = lo;
-          *reinterpret_cast<u32x2*>(sV + (dim + 1) * C::VSTR + 4 * kq) = hi;
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 a = lds128(kr + koff[ks]);
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) sacc[kb2][rb] = mfma_bf16(a, qb[rb][ks], sacc[kb2][rb]);
         }
       } else {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const u32x4 col = {v[it][0][m], v[it][1][m], v[it][2][m], v[it][3][m]};
-          *reinterpret_cast<u32x4*>(sV + (ch * 4 + m) * C::VSTR + 4 * kq) = col;
+        for (int c4 = 0; c4 < KS / 4; ++c4) {
+          const u32x4 a4 = lds128(kr + koff[c4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+              sacc[kb2][rb] = mfma_f32(__uint_as_float(a4[e]), qf[rb][4 * c4 + e], sacc[kb2][rb]);
         }
       }
+    }
+    // counts in the layout of S^T
+    if constexpr (PL) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const int kb = 2 * kc + kb2;
+        if constexpr (KIND == KIND_NEAR) {
+          const int jrel0 = j0 - r0 + 16 * kb;
+          const int cm = min((jrel0 + 15) >> 5, chmax);
+#pragma unroll
+          for (int ch = 0; ch < 4; ++ch) {
+            if (ch > cm) break;
+            const u32x4 th = lds128(sTh + 16 * clamp08(jrel0 + l16 - 32 * ch - 8 * g + 1));
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) cacc[kb2][rb] = mfma_bf16(th, cnt_b[rb][ch], cacc[kb2][rb]);
+          }
+        } else {
+#pragma unroll
+          for (int ch = 0; ch < NCH; ++ch) {
+            const u32x4 th = lds128(sTh + 16 * clamp08(mkey[kb] - 32 * ch - 8 * g));
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) cacc[kb2][rb] = mfma_bf16(th, cnt_b[rb][ch], cacc[kb2][rb]);
+          }
+        }
+      }
+    }
+    // weights in log2 units (ALiBi) or logits (PLSH); masking; local maxima
+    float lmx[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int J = jc + 16 * kb2 + 4 * g + e;
+          float x = sacc[kb2][rb][e];
+          if constexpr (MODE == MODE_ALIBI) x = fmaf(x, sc, -beta * fabsf(static_cast<float>(R[rb] - J)));
+          bool ok = true;
+          if constexpr (KIND == KIND_NEAR) {
+            if constexpr (PL) ok = cacc[kb2][rb][e] > 0.5f;
+            else ok = J < n;
+            if constexpr (CAUSAL) ok = ok && J <= R[rb];
+            x = ok ? x : -INFINITY;
+          } else {
+            if (need_mask) {
+              if constexpr (PL) ok = cacc[kb2][rb][e] > 0.5f;
+              else ok = J < n;
+              x = ok ? x : -INFINITY;
+            }
+          }
+          sacc[kb2][rb][e] = x;
+          lmx[rb] = fmaxf(lmx[rb], x);
+        }
+    // raise the running maximum only when some row outgrows it by the margin
+    const bool grow = lmx[0] > Mrow[0] + thr || lmx[1] > Mrow[1] + thr;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const float mn = fmaxf(Mrow[rb], xmax16(lmx[rb]));
+        const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((Mrow[rb] - mn) * scp);
+        Mrow[rb] = mn;
+        Msc[rb] = mn == -INFINITY ? 0.0f : mn * scp;
+        lsum[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db][rb] *= alpha;
+      }
+    }
+    // weights and the value product O^T += V^T P^T
+    if constexpr (BF) {
+      u32x4 pf[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float p[2][4];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float x = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][rb][e], scp, -Msc[rb]));
+            if constexpr (PL) x *= cacc[kb2][rb][e];
+            p[kb2][e] = x;
+            lsum[rb] += x;
+          }
+        pf[rb] = u32x4{pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]), pack_bf16(p[1][0], p[1][1]),
+                       pack_bf16(p[1][2], p[1][3])};
+      }
+      const unsigned char* vb = sV + (32 * kc) * G::RB;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x2 v0 = lds_tr16(vb + vtr[db]);
+        const u32x2 v1 = lds_tr16(vb + 16 * G::RB + vtr[db]);
+        const u32x4 a = {v0[0], v0[1], v1[0], v1[1]};
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) acc[db][rb] = mfma_bf16(a, pf[rb], acc[db][rb]);
+      }
+    } else {
+      float p[2][2][4];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float x = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][rb][e], scp, -Msc[rb]));
+            if constexpr (PL) x *= cacc[kb2][rb][e];
+            p[rb][kb2][e] = x;
+            lsum[rb] += x;
+          }
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = 32 * kc + 16 * kb2 + 4 * g + e;
+          const unsigned char* vrow = sV + key * G::RB + 4 * (l16 & 3);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const int c = (4 * db + (l16 >> 2)) ^ G::swv(key);
+            const float va = *reinterpret_cast<const float*>(vrow + 16 * c);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) acc[db][rb] = mfma_f32(va, p[rb][kb2][e], acc[db][rb]);
+          }
+        }
     }
   }
 };
 
 template <int D, bool BF, bool CAUSAL, int NCH, int MODE>
-__global__ __launch_bounds__(NT, (Cfg<D, BF, MODE>::LDS > 80 * 1024 ? 1 : 2)) void fwd_kernel(FwdArgs A, HeadOrder ord,
-                                                                                     HeadScale hsc) {
-  using C = Cfg<D, BF, MODE>;
-  using T = typename C::T;
+__global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2)) void fwd_kernel(FwdArgs A,
+                                                                                              HeadOrder ord,
+                                                                                              HeadScale hsc) {
+  using G = Geo<D, BF>;
+  using T = typename G::T;
+  using F = Fwd<D, BF, CAUSAL, NCH, MODE>;
   constexpr bool PL = MODE == MODE_PLSH;
-  constexpr int KS = C::KS, DB = C::DB;
+  constexpr int KS = G::KS, DB = G::DB;
 
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  T* sKb = reinterpret_cast<T*>(smem);
-  T* sVb = sKb + 2 * C::K_ELEMS;
-  uint16_t* sH = reinterpret_cast<uint16_t*>(smem);
-  unsigned char* sm = smem + C::BIG;
-  PlanRec* sRec = reinterpret_cast<PlanRec*>(sm);
-  int* sAa = reinterpret_cast<int*>(sm + MAXS * 32);  // a_i sorted ascending
-  int* sAe = sAa + MAXS;                             // e_i in that order
-  int* sEe = sAe + MAXS;                             // e2_i sorted descending
-  int* sEa = sEe + MAXS;                             // a2_i in that order
-  u32x4* sTh = reinterpret_cast<u32x4*>(sEa + MAXS); // thermometer patterns
-  int* sSc = reinterpret_cast<int*>(sTh + 9);         // window scalars
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  unsigned char* stage0 = smem;
+  unsigned char* stage1 = smem + G::STAGE;
+  unsigned char* hc = stage1;  // near counts live in stage 1 until the prologue ends
+  unsigned char* sm = smem + G::BIG;
+  PlanRec* sRec = reinterpret_cast<PlanRec*>(sm + SM_REC);
+  int* sAa = reinterpret_cast<int*>(sm + SM_AA);
+  int* sAe = reinterpret_cast<int*>(sm + SM_AE);
+  int* sEe = reinterpret_cast<int*>(sm + SM_EE);
+  int* sEa = reinterpret_cast<int*>(sm + SM_EA);
+  int* sSc = reinterpret_cast<int*>(sm + SM_SC);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l16 = lane & 15, g = lane >> 4;
+  F f;
+  const int tid = threadIdx.x;
+  f.lane = tid & 63;
+  f.l16 = f.lane & 15;
+  f.g = f.lane >> 4;
+  f.w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = f.lane, l16 = f.l16, g = f.g, w = f.w;
+  f.sTh = sm + SM_TH;
 
-  // ---- work item: XCD-aware order (consecutive tiles of a head share an XCD)
+  // ---- work item: consecutive tiles of a head stay on one XCD
   const int gid = blockIdx.x;
   const int xcd = gid & 7, kk = gid >> 3;
   const int inst = kk / A.cs;
@@ -221,95 +419,64 @@ __global__ __launch_bounds__(NT, (Cfg<D, BF, MODE>::LDS > 80 * 1024 ? 1 : 2)) vo
   const int r0 = qt * BM;
   const int nrows = min(BM, n - r0);
   const int rlast = r0 + nrows - 1;
-  const T* __restrict__ Qp = static_cast<const T*>(A.q) + static_cast<size_t>(b * A.Hq + h) * n * D;
-  const T* __restrict__ Kp = static_cast<const T*>(A.k) + static_cast<size_t>(b * A.Hkv + kvh) * n * D;
-  const T* __restrict__ Vp = static_cast<const T*>(A.v) + static_cast<size_t>(b * A.Hkv + kvh) * n * D;
-  T* __restrict__ Op = static_cast<T*>(A.o) + static_cast<size_t>(b * A.Hq + h) * n * D;
+  const T* Qp = static_cast<const T*>(A.q) + static_cast<size_t>(b * A.Hq + h) * n * D;
+  const T* Kh = static_cast<const T*>(A.k) + static_cast<size_t>(b * A.Hkv + kvh) * n * D;
+  const T* Vh = static_cast<const T*>(A.v) + static_cast<size_t>(b * A.Hkv + kvh) * n * D;
+  T* Op = static_cast<T*>(A.o) + static_cast<size_t>(b * A.Hq + h) * n * D;
 
-  // rows of this lane: R[rb] = r0 + 32 w + 16 rb + l16 (relative: rr[rb])
-  int rr[2], R[2];
+  // first tile (the query rows' own keys) starts loading right away
+  TileLoader<D, BF> ld;
+  ld.init(w, lane);
+  ld.issue(Kh, Vh, r0, n, stage0, w);
+
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    rr[rb] = 32 * w + 16 * rb + l16;
-    R[rb] = r0 + rr[rb];
+    f.rr[rb] = 32 * w + 16 * rb + l16;
+    f.R[rb] = r0 + f.rr[rb];
   }
-
-  // ---- Q fragments (operand B of S^T = K Q^T)
-  u32x4 qb[2][BF ? KS : 1];
-  float qf[2][BF ? 1 : KS];
+  // Q fragments (operand B of S^T = K Q^T)
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    const bool ok = R[rb] < n;
-    const T* qrow = Qp + static_cast<size_t>(ok ? R[rb] : 0) * D;
+    const bool ok = f.R[rb] < n;
+    const T* qrow = Qp + static_cast<size_t>(ok ? f.R[rb] : 0) * D;
     if constexpr (BF) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qb[rb][ks] = ok ? *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g) : u32x4{0, 0, 0, 0};
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
+        f.qb[rb][ks] = ok ? x : u32x4{0, 0, 0, 0};
+      }
     } else {
 #pragma unroll
       for (int c4 = 0; c4 < KS / 4; ++c4) {
-        const u32x4 x = ok ? *reinterpret_cast<const u32x4*>(qrow + KS * g + 4 * c4) : u32x4{0, 0, 0, 0};
+        const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + KS * g + 4 * c4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) qf[rb][4 * c4 + e] = __uint_as_float(x[e]);
+        for (int e = 0; e < 4; ++e) f.qf[rb][4 * c4 + e] = ok ? __uint_as_float(x[e]) : 0.0f;
       }
     }
   }
+  f.init_offsets();
 
-  // ---- window of keys that can carry weight
+  // ---- window of keys that can carry weight; count operands
   int lo, hi, afull = INT_MAX, efull = INT_MIN, cntA = 0;
-  u32x4 hf[2][PL ? 4 : 1];          // near counts H (operand B), [rb][position chunk]
-  u32x4 ufl[2][PL ? NCH : 1];       // left:  [r < e_slot]
-  u32x4 ufr[2][PL && !CAUSAL ? NCH : 1];  // right: [r >= a2_slot]
+  u32x4 hf[2][4];                          // near: H (operand B) per position chunk
+  u32x4 ufl[2][PL ? NCH : 1];              // left:  [r < e_slot]
+  u32x4 ufr[2][(PL && !CAUSAL) ? NCH : 1]; // right: [r >= a2_slot]
+  int va0 = INT_MAX, va1 = INT_MAX;        // sorted a_i (lane k: k-th, k-64-th)
+  int ve0 = INT_MIN, ve1 = INT_MIN;        // e2_i sorted descending
   if constexpr (PL) {
+    // zero the near-count matrix (stage 1, not yet in use)
+    for (int x = tid; x < G::HC / 16; x += NT) reinterpret_cast<u32x4*>(hc)[x] = u32x4{0, 0, 0, 0};
     if (tid < s) sRec[tid] = A.plan[(static_cast<size_t>(h) * A.ntile + qt) * s + tid];
     if (tid < 9) {
       u32x4 p;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        p[q] = (tid >= 2 * q + 2) ? 0x3F803F80u : (tid == 2 * q + 1 ? 0x00003F80u : 0u);
-      sTh[tid] = p;
+      for (int q = 0; q < 4; ++q) p[q] = (tid >= 2 * q + 2) ? 0x3F803F80u : (tid == 2 * q + 1 ? 0x00003F80u : 0u);
+      *reinterpret_cast<u32x4*>(sm + SM_TH + 16 * tid) = p;
     }
-    for (int x = tid; x < C::H_BYTES / 16; x += NT) reinterpret_cast<u32x4*>(sH)[x] = u32x4{0, 0, 0, 0};
     __syncthreads();
-    if (tid < s) {
-      const PlanRec me = sRec[tid];
-      int rk = 0, rk2 = 0;
-      for (int k2 = 0; k2 < s; ++k2) {
-        const int ak = sRec[k2].a, ek = sRec[k2].e2;
-        rk += (ak < me.a) || (ak == me.a && k2 < tid);
-        rk2 += (ek > me.e2) || (ek == me.e2 && k2 < tid);
-      }
-      sAa[rk] = me.a;
-      sAe[rk] = me.e;
-      sEe[rk2] = me.e2;
-      sEa[rk2] = me.a2;
-    }
-    if (w == 0) {
-      int vlo = INT_MAX, vhi = INT_MIN, vaf = INT_MAX, vef = INT_MIN, vca = 0;
-      for (int i = lane; i < s; i += 64) {
-        const PlanRec& Rr = sRec[i];
-        vlo = min(vlo, Rr.a);
-        vhi = max(vhi, Rr.e2);
-        if (Rr.e > rlast) vaf = min(vaf, Rr.a);
-        if (Rr.a2 <= r0) vef = max(vef, Rr.e2);
-        vca += Rr.a < r0;
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        vlo = min(vlo, __shfl_xor(vlo, o, 64));
-        vhi = max(vhi, __shfl_xor(vhi, o, 64));
-        vaf = min(vaf, __shfl_xor(vaf, o, 64));
-        vef = max(vef, __shfl_xor(vef, o, 64));
-        vca += __shfl_xor(vca, o, 64);
-      }
-      if (lane == 0) {
-        sSc[0] = vlo; sSc[1] = vhi; sSc[2] = vaf; sSc[3] = vef; sSc[4] = vca;
-      }
-    }
-    // near counts: thread p owns row r0 + p of H
-    if (tid < BM) {
+    if (w < 2) {
+      // near counts: thread p owns row r0 + p (column p of the [position][row] matrix)
       const int p = tid, wp = p >> 5, bp = p & 31;
-      uint16_t* Hrow = sH + p * C::HSTR;
       for (int i = 0; i < s; ++i) {
         const u32x4 bw = *reinterpret_cast<const u32x4*>(sRec[i].bits);
         int st = 0, en = BM;
@@ -317,54 +484,111 @@ __global__ __launch_bounds__(NT, (Cfg<D, BF, MODE>::LDS > 80 * 1024 ? 1 : 2)) vo
         for (int q = 0; q < 4; ++q) {
           const uint32_t le = q < wp ? 0xFFFFFFFFu : (q == wp ? (0xFFFFFFFFu >> (31 - bp)) : 0u);
           const uint32_t m = bw[q] & le;
-          if (m) st = 32 * q + 31 - __clz(m);
+          st = m ? 32 * q + 31 - __builtin_clz(m) : st;
         }
 #pragma unroll
         for (int q = 3; q >= 0; --q) {
           const uint32_t gt = q > wp ? 0xFFFFFFFFu : (q == wp ? (bp == 31 ? 0u : (0xFFFFFFFEu << bp)) : 0u);
           const uint32_t m = bw[q] & gt;
-          if (m) en = 32 * q + __ffs(m) - 1;
+          en = m ? 32 * q + __builtin_ctz(m) : en;
         }
-        Hrow[st] = f32_to_bf16_exact(bf16_bits_to_f32(Hrow[st]) + 1.0f);
-        if (en < BM) Hrow[en] = f32_to_bf16_exact(bf16_bits_to_f32(Hrow[en]) - 1.0f);
+        uint16_t* cs = reinterpret_cast<uint16_t*>(hc + st * (2 * BM) + 2 * p);
+        *cs = static_cast<uint16_t>(__float_as_uint(__uint_as_float(static_cast<uint32_t>(*cs) << 16) + 1.0f) >> 16);
+        if (en < BM) {
+          uint16_t* ce = reinterpret_cast<uint16_t*>(hc + en * (2 * BM) + 2 * p);
+          *ce = static_cast<uint16_t>(__float_as_uint(__uint_as_float(static_cast<uint32_t>(*ce) << 16) - 1.0f) >> 16);
+        }
+      }
+    } else {
+      // ranks of the hashes by a (wave 2) and by e2 descending (wave 3)
+      for (int i = lane; i < s; i += 64) {
+        const PlanRec me = sRec[i];
+        int rk = 0;
+        if (w == 2) {
+          for (int k2 = 0; k2 < s; ++k2) {
+            const int ak = sRec[k2].a;
+            rk += (ak < me.a) || (ak == me.a && k2 < i);
+          }
+          sAa[rk] = me.a;
+          sAe[rk] = me.e;
+        } else {
+          for (int k2 = 0; k2 < s; ++k2) {
+            const int ek = sRec[k2].e2;
+            rk += (ek > me.e2) || (ek == me.e2 && k2 < i);
+          }
+          sEe[rk] = me.e2;
+          sEa[rk] = me.a2;
+        }
+      }
+      if (w == 2) {
+        int vlo = INT_MAX, vhi = INT_MIN, vaf = INT_MAX, vef = INT_MIN, vca = 0;
+        for (int i = lane; i < s; i += 64) {
+          const PlanRec& Rr = sRec[i];
+          vlo = min(vlo, Rr.a);
+          vhi = max(vhi, Rr.e2);
+          if (Rr.e > rlast) vaf = min(vaf, Rr.a);
+          if (Rr.a2 <= r0) vef = max(vef, Rr.e2);
+          vca += Rr.a < r0;
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+          vlo = min(vlo, __shfl_xor(vlo, o, 64));
+          vhi = max(vhi, __shfl_xor(vhi, o, 64));
+          vaf = min(vaf, __shfl_xor(vaf, o, 64));
+          vef = max(vef, __shfl_xor(vef, o, 64));
+          vca += __shfl_xor(vca, o, 64);
+        }
+        if (lane == 0) {
+          sSc[0] = vlo; sSc[1] = vhi; sSc[2] = vaf; sSc[3] = vef; sSc[4] = vca;
+        }
       }
     }
     __syncthreads();
+    // H operand through transposing reads of the [position][row] matrix:
+    // source lane a + 4t of a 16-lane group reads rows 4a..4a+3 at position p0 + t
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int ch = 0; ch < 4; ++ch)
-        hf[rb][ch] = *reinterpret_cast<const u32x4*>(sH + rr[rb] * C::HSTR + 32 * ch + 8 * g);
-    // count operands for the side tiles
+      for (int ch = 0; ch < 4; ++ch) {
+        const int p0 = 32 * ch + 8 * g;
+        const unsigned char* base = hc + (p0 + (l16 >> 2)) * (2 * BM) + 2 * (32 * w + 16 * rb + 4 * (l16 & 3));
+        const u32x2 x0 = lds_tr16(base);
+        const u32x2 x1 = lds_tr16(base + 4 * (2 * BM));
+        hf[rb][ch] = u32x4{x0[0], x0[1], x1[0], x1[1]};
+      }
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
-        u32x4 f = {0, 0, 0, 0}, f2 = {0, 0, 0, 0};
+        u32x4 fl = {0, 0, 0, 0}, fr = {0, 0, 0, 0};
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const int slot = 32 * ch + 8 * g + t;
-          const bool in = slot < s;
           const uint32_t one = 0x3F80u << (16 * (t & 1));
-          if (in && R[rb] < sAe[slot]) f[t >> 1] |= one;
-          if (!CAUSAL && in && R[rb] >= sEa[slot]) f2[t >> 1] |= one;
+          if (slot < s && f.R[rb] < sAe[slot]) fl[t >> 1] |= one;
+          if (!CAUSAL && slot < s && f.R[rb] >= sEa[slot]) fr[t >> 1] |= one;
         }
-        ufl[rb][ch] = f;
-        if constexpr (!CAUSAL) ufr[rb][ch] = f2;
+        ufl[rb][ch] = fl;
+        if constexpr (!CAUSAL) ufr[rb][ch] = fr;
       }
     }
-    lo = sSc[0];
-    hi = sSc[1];
-    afull = sSc[2];
-    efull = sSc[3];
-    cntA = sSc[4];
-    __syncthreads();  // H region is reused for K/V from here on
+    va0 = lane < s ? sAa[lane] : INT_MAX;
+    va1 = lane + 64 < s ? sAa[lane + 64] : INT_MAX;
+    if constexpr (!CAUSAL) {
+      ve0 = lane < s ? sEe[lane] : INT_MIN;
+      ve1 = lane + 64 < s ? sEe[lane + 64] : INT_MIN;
+    }
+    lo = __builtin_amdgcn_readfirstlane(sSc[0]);
+    hi = __builtin_amdgcn_readfirstlane(sSc[1]);
+    afull = __builtin_amdgcn_readfirstlane(sSc[2]);
+    efull = __builtin_amdgcn_readfirstlane(sSc[3]);
+    cntA = __builtin_amdgcn_readfirstlane(sSc[4]);
   } else {
     lo = 0;
     hi = n;
   }
 
-  // ---- tile list
+  // ---- tile schedule
   const int nnear = nrows > BN ? 2 : 1;
   const int nleft = lo < r0 ? (r0 - lo + BN - 1) / BN : 0;
   const int nright = (!CAUSAL && hi > r0 + BM) ? (hi - (r0 + BM) + BN - 1) / BN : 0;
@@ -375,254 +599,122 @@ __global__ __launch_bounds__(NT, (Cfg<D, BF, MODE>::LDS > 80 * 1024 ? 1 : 2)) vo
   };
 
   // ---- softmax state
-  const float sc = rsqrtf(static_cast<float>(D)) * kLog2e;   // logit -> log2 units
-  const float scp = MODE == MODE_PLSH ? sc : 1.0f;            // scale applied at exp time
-  const float thr = 8.0f / scp;                               // rescale threshold (logit units)
-  const float beta = MODE == MODE_ALIBI ? hsc.beta[h] : 0.0f;
-  float Mrow[2] = {-INFINITY, -INFINITY}, Msc[2] = {0.f, 0.f}, lsum[2] = {0.f, 0.f};
-  f32x4 acc[DB][2];
+  f.sc = rsqrtf(static_cast<float>(D)) * kLog2e;  // logit -> log2 units
+  f.scp = PL ? f.sc : 1.0f;                        // scale applied at exp time
+  f.thr = 8.0f / f.scp;                            // rescale margin (units of x)
+  f.beta = MODE == MODE_ALIBI ? hsc.beta[h] : 0.0f;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int rb = 0; rb < 2; ++rb) {
+    f.Mrow[rb] = -INFINITY;
+    f.Msc[rb] = 0.f;
+    f.lsum[rb] = 0.f;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) acc[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < DB; ++db) f.acc[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
-  // side-tile count state (uniform)
-  int lcnt_hi = cntA, rA = s, rB = s;
-
-  Tile<D, BF, MODE> tl;
-  tl.load(Kp, Vp, tile_j0(0), n, tid);
-  tl.store(sKb, sVb, tid);
-  __syncthreads();
-
-  for (int t = 0; t < ntl; ++t) {
-    const int buf = t & 1;
-    const T* sK = sKb + buf * C::K_ELEMS;
-    const T* sV = sVb + buf * C::V_ELEMS;
-    const int j0 = tile_j0(t);
-    const int kind = t < nnear ? KIND_NEAR : (t < nnear + nleft ? KIND_LEFT : KIND_RIGHT);
-    if (t + 1 < ntl) tl.load(Kp, Vp, tile_j0(t + 1), n, tid);
-
-    // per-lane count of sorted hashes active at this lane's key of each 16-key block
-    int mkey[4] = {0, 0, 0, 0};
-    if constexpr (PL) {
-      if (kind == KIND_LEFT) {
+  // ---- tile loop, in three phases so that each phase's count operands die
+  // with it.  Tile t has landed when iteration t starts (issued one
+  // iteration earlier); after the barrier every wave is done with tile t-1,
+  // whose stage then receives tile t+1.
+  auto begin_tile = [&](int t) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 1 < ntl) ld.issue(Kh, Vh, tile_j0(t + 1), n, (t & 1) ? stage0 : stage1, w);
+  };
+  int t = 0;
+  {
+    const int mkey0[4] = {0, 0, 0, 0};
+    const int chmax = CAUSAL ? w : 3;
+    for (; t < nnear; ++t) {
+      begin_tile(t);
+      const int j0 = tile_j0(t);
+      const unsigned char* st = (t & 1) ? stage1 : stage0;
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        if (CAUSAL && j0 + 32 * kc > r0 + 32 * w + 31) continue;
+        f.template chunk<KIND_NEAR>(st, st + G::TILE, j0, r0, n, kc, true, mkey0, hf, chmax);
+      }
+    }
+  }
+  {
+    u32x4 cb[2][4];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) cb[rb][ch] = PL && ch < NCH ? ufl[rb][ch < NCH ? ch : 0] : u32x4{0, 0, 0, 0};
+    int lcnt_hi = cntA;
+    for (; t < nnear + nleft; ++t) {
+      begin_tile(t);
+      const int j0 = tile_j0(t);
+      const unsigned char* st = (t & 1) ? stage1 : stage0;
+      int mkey[4] = {0, 0, 0, 0};
+      bool need_mask = false;
+      if constexpr (PL) {
+        // hashes whose block start a lies in this tile: a in [j0, j0 + 64)
         int clo = lcnt_hi;
-        while (clo > 0 && sAa[clo - 1] >= j0) --clo;
+        while (clo > 0) {
+          const int x = clo - 1;
+          const int av = __builtin_amdgcn_readlane(x < 64 ? va0 : va1, x & 63);
+          if (av < j0) break;
+          clo = x;
+        }
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) mkey[kb] = clo;
         for (int x = clo; x < lcnt_hi; ++x) {
-          const int av = sAa[x];
+          const int av = __builtin_amdgcn_readlane(x < 64 ? va0 : va1, x & 63);
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) mkey[kb] += (j0 + 16 * kb + l16 >= av);
         }
         lcnt_hi = clo;
-      } else if (!CAUSAL && kind == KIND_RIGHT) {
-        while (rA > 0 && sEe[rA - 1] < j0 + BN) --rA;
-        while (rB > 0 && sEe[rB - 1] <= j0) --rB;
+        need_mask = j0 < afull;
+      }
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) f.template chunk<KIND_LEFT>(st, st + G::TILE, j0, r0, n, kc, need_mask, mkey, cb, 0);
+    }
+  }
+  if constexpr (!CAUSAL) {
+    u32x4 cb[2][4];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) cb[rb][ch] = PL && ch < NCH ? ufr[rb][ch < NCH ? ch : 0] : u32x4{0, 0, 0, 0};
+    int rA = s, rB = s;
+    for (; t < ntl; ++t) {
+      begin_tile(t);
+      const int j0 = tile_j0(t);
+      const unsigned char* st = (t & 1) ? stage1 : stage0;
+      int mkey[4] = {0, 0, 0, 0};
+      bool need_mask;
+      if constexpr (PL) {
+        while (rA > 0 && __builtin_amdgcn_readlane(rA - 1 < 64 ? ve0 : ve1, (rA - 1) & 63) < j0 + BN) --rA;
+        while (rB > 0 && __builtin_amdgcn_readlane(rB - 1 < 64 ? ve0 : ve1, (rB - 1) & 63) <= j0) --rB;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) mkey[kb] = rA;
         for (int x = rA; x < rB; ++x) {
-          const int ev = sEe[x];
+          const int ev = __builtin_amdgcn_readlane(x < 64 ? ve0 : ve1, x & 63);
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) mkey[kb] += (ev > j0 + 16 * kb + l16);
         }
-      }
-    }
-    bool need_mask;
-    if constexpr (PL)
-      need_mask = kind == KIND_NEAR || (kind == KIND_LEFT && j0 < afull) || (kind == KIND_RIGHT && j0 + BN > efull);
-    else
-      need_mask = kind == KIND_NEAR || j0 < 0 || j0 + BN > n;
-
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const int jc = j0 + 32 * kc;
-      // causal: skip key chunks entirely above this wave's last row
-      if (CAUSAL && kind == KIND_NEAR && jc > r0 + 32 * w + 31) continue;
-
-      f32x4 sacc[2][2], cacc[2][2];
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          sacc[x][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          cacc[x][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-      // S^T = K Q^T
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const int kb = 2 * kc + kb2;
-        const T* krow = sK + (16 * kb + l16) * C::KSTR;
-        if constexpr (BF) {
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(krow + 32 * ks + 8 * g);
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) sacc[kb2][rb] = mfma_bf16(a, qb[rb][ks], sacc[kb2][rb]);
-          }
-        } else {
-#pragma unroll
-          for (int c4 = 0; c4 < KS / 4; ++c4) {
-            const u32x4 a4 = *reinterpret_cast<const u32x4*>(krow + KS * g + 4 * c4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-              for (int rb = 0; rb < 2; ++rb)
-                sacc[kb2][rb] = mfma_f32(__uint_as_float(a4[e]), qf[rb][4 * c4 + e], sacc[kb2][rb]);
-          }
-        }
-      }
-      // counts c^T in the layout of S^T
-      if constexpr (PL) {
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-          const int kb = 2 * kc + kb2;
-          if (kind == KIND_NEAR) {
-            const int jrel0 = j0 - r0 + 16 * kb;          // first key of the block, relative to r0
-            const int jrel = jrel0 + l16;
-            int chmax = (jrel0 + 15) >> 5;
-            if (CAUSAL) chmax = min(chmax, w);
-#pragma unroll
-            for (int ch = 0; ch < 4; ++ch) {
-              if (ch > chmax) break;
-              const u32x4 th = sTh[clamp08(jrel - 32 * ch - 8 * g + 1)];
-#pragma unroll
-              for (int rb = 0; rb < 2; ++rb) cacc[kb2][rb] = mfma_bf16(th, hf[rb][ch], cacc[kb2][rb]);
-            }
-          } else if (kind == KIND_LEFT) {
-#pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) {
-              const u32x4 th = sTh[clamp08(mkey[kb] - 32 * ch - 8 * g)];
-#pragma unroll
-              for (int rb = 0; rb < 2; ++rb) cacc[kb2][rb] = mfma_bf16(th, ufl[rb][ch], cacc[kb2][rb]);
-            }
-          } else if constexpr (!CAUSAL) {
-#pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) {
-              const u32x4 th = sTh[clamp08(mkey[kb] - 32 * ch - 8 * g)];
-#pragma unroll
-              for (int rb = 0; rb < 2; ++rb) cacc[kb2][rb] = mfma_bf16(th, ufr[rb][ch], cacc[kb2][rb]);
-            }
-          }
-        }
-      }
-      // masking and the tile's row maxima
-      float tmx[2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int J = jc + 16 * kb2 + 4 * g + e;
-            float x = sacc[kb2][rb][e];
-            if constexpr (MODE == MODE_ALIBI) {
-              const float dist = fabsf(static_cast<float>(R[rb] - J));
-              x = fmaf(x, sc, -beta * dist);
-            }
-            if (need_mask) {
-              bool ok;
-              if constexpr (PL)
-                ok = cacc[kb2][rb][e] > 0.5f;
-              else
-                ok = J >= 0 && J < n;
-              if (CAUSAL && kind == KIND_NEAR) ok = ok && (J <= R[rb]);
-              x = ok ? x : -INFINITY;
-            }
-            sacc[kb2][rb][e] = x;
-            mx = fmaxf(mx, x);
-          }
-        }
-        tmx[rb] = xmax16(mx);
-      }
-      const bool grow = tmx[0] > Mrow[0] + thr || tmx[1] > Mrow[1] + thr;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          const float mn = fmaxf(Mrow[rb], tmx[rb]);
-          const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((Mrow[rb] - mn) * scp);
-          Mrow[rb] = mn;
-          Msc[rb] = mn == -INFINITY ? 0.0f : mn * scp;
-          lsum[rb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) acc[db][rb] *= alpha;
-        }
-      }
-      // weights and the value product O^T += V^T P^T
-      if constexpr (BF) {
-        u32x4 pf[2];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          float p[2][4];
-#pragma unroll
-          for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              float x = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][rb][e], scp, -Msc[rb]));
-              if constexpr (PL) x *= cacc[kb2][rb][e];
-              p[kb2][e] = x;
-              lsum[rb] += x;
-            }
-          pf[rb] = u32x4{pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]), pack_bf16(p[1][0], p[1][1]),
-                         pack_bf16(p[1][2], p[1][3])};
-        }
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const T* vrow = sV + (16 * db + l16) * C::VSTR + 32 * kc + 4 * g;
-          const u32x2 v0 = *reinterpret_cast<const u32x2*>(vrow);
-          const u32x2 v1 = *reinterpret_cast<const u32x2*>(vrow + 16);
-          const u32x4 a = {v0[0], v0[1], v1[0], v1[1]};
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) acc[db][rb] = mfma_bf16(a, pf[rb], acc[db][rb]);
-        }
+        need_mask = j0 + BN > efull;
       } else {
-        float p[2][2][4];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              float x = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][rb][e], scp, -Msc[rb]));
-              if constexpr (PL) x *= cacc[kb2][rb][e];
-              p[rb][kb2][e] = x;
-              lsum[rb] += x;
-            }
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-#pragma unroll
-          for (int kb2 = 0; kb2 < 2; ++kb2) {
-            const u32x4 a4 =
-                *reinterpret_cast<const u32x4*>(sV + (16 * db + l16) * C::VSTR + 32 * kc + 16 * kb2 + 4 * g);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-              for (int rb = 0; rb < 2; ++rb)
-                acc[db][rb] = mfma_f32(__uint_as_float(a4[e]), p[rb][kb2][e], acc[db][rb]);
-          }
-        }
+        need_mask = j0 + BN > n;
       }
-    }
-
-    if (t + 1 < ntl) {
-      // buf ^ 1 was last read in the previous iteration, which every wave left
-      // through the barrier below; one barrier per tile publishes the store.
-      tl.store(sKb + (buf ^ 1) * C::K_ELEMS, sVb + (buf ^ 1) * C::V_ELEMS, tid);
-      __syncthreads();
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+        f.template chunk<KIND_RIGHT>(st, st + G::TILE, j0, r0, n, kc, need_mask, mkey, cb, 0);
     }
   }
 
   // ---- epilogue: O_r = acc / l
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    const float l = xsum16(lsum[rb]);
+    const float l = xsum16(f.lsum[rb]);
     const float inv = 1.0f / l;
-    if (R[rb] >= n) continue;
-    T* orow = Op + static_cast<size_t>(R[rb]) * D;
+    if (f.R[rb] >= n) continue;
+    T* orow = Op + static_cast<size_t>(f.R[rb]) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const f32x4 o = acc[db][rb] * inv;
+      const f32x4 o = f.acc[db][rb] * inv;
       if constexpr (BF) {
         *reinterpret_cast<u32x2*>(orow + 16 * db + 4 * g) = u32x2{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
       } else {
@@ -634,16 +726,16 @@ __global__ __launch_bounds__(NT, (Cfg<D, BF, MODE>::LDS > 80 * 1024 ? 1 : 2)) vo
 
 template <int D, bool BF, bool CAUSAL, int NCH, int MODE>
 hipError_t launch_one(const FwdArgs& a, const HeadOrder& ord, const HeadScale& hs, int grid, hipStream_t st) {
-  using C = Cfg<D, BF, MODE>;
+  constexpr int lds = Geo<D, BF>::BIG + SMALL;
   auto kfn = fwd_kernel<D, BF, CAUSAL, NCH, MODE>;
   static bool attr_done = false;  // benign race: idempotent
-  if (C::LDS > 64 * 1024 && !attr_done) {
+  if (lds > 64 * 1024 && !attr_done) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_done = true;
   }
-  hipLaunchKernelGGL(kfn, dim3(grid), dim3(NT), C::LDS, st, a, ord, hs);
+  hipLaunchKernelGGL(kfn, dim3(grid), dim3(NT), lds, st, a, ord, hs);
   return hipGetLastError();
 }
 
