@@ -67,7 +67,6 @@ constexpr int NT = 256;    // threads per workgroup
 constexpr int NW = 4;      // waves per workgroup
 constexpr int BM = 128;    // query rows per workgroup
 constexpr int BN = 64;     // keys per tile
-constexpr int MAXS = 128;  // hashes per head
 constexpr float kLog2e = 1.4426950408889634f;
 
 enum { MODE_PLSH = 0, MODE_ALIBI = 1 };
@@ -79,7 +78,8 @@ struct HeadScale { float beta[256]; };   // log2(e) / sigma_h (dense ALiBi)
 struct FwdArgs {
   const void* q; const void* k; const void* v; void* o;
   const PlanRec* plan;
-  int B, Hq, Hkv, n, s, ntile, cs;
+  const int* meta;  // tile summaries, mstride ints each
+  int B, Hq, Hkv, n, s, ntile, cs, mstride;
 };
 
 template <int D, bool BF>
@@ -92,7 +92,7 @@ struct Geo {
   static constexpr int TILE = BN * RB;               // bytes of one K or V tile
   static constexpr int NI = TILE / 1024 / NW;        // load instructions per wave per matrix
   static constexpr int STAGE = 2 * TILE;             // K tile + V tile
-  static constexpr int HC = BM * BM * 2;             // near counts, bf16 [p][r]
+  static constexpr int HC = (BM + 1) * BM * 2;       // near counts, bf16 [p][r], p <= 128
   static constexpr int BIG = 2 * STAGE > STAGE + HC ? 2 * STAGE : STAGE + HC;
   static constexpr int KS = BF ? D / 32 : D / 4;     // k-steps of the logit product
   static constexpr int DB = D / 16;                  // 16-wide output column blocks
@@ -100,15 +100,9 @@ struct Geo {
   __device__ static int swv(int key) { return CPR >= 16 ? 2 * (key & 7) : 2 * (key & 3); }
 };
 
-// small-LDS region: plan records, sorted hash arrays, prefix table, scalars
-constexpr int SM_REC = 0;
-constexpr int SM_AA = SM_REC + MAXS * 32;  // a_i sorted ascending
-constexpr int SM_AE = SM_AA + MAXS * 4;    // e_i in that order
-constexpr int SM_EE = SM_AE + MAXS * 4;    // e2_i sorted descending
-constexpr int SM_EA = SM_EE + MAXS * 4;    // a2_i in that order
-constexpr int SM_TH = SM_EA + MAXS * 4;    // 9 x 16-byte bf16 prefixes of ones
-constexpr int SM_SC = SM_TH + 9 * 16;      // scalars
-constexpr int SMALL = SM_SC + 64;
+// small-LDS region: the 9 x 16-byte bf16 prefixes of ones
+constexpr int SM_TH = 0;
+constexpr int SMALL = 256;
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -130,6 +124,30 @@ __device__ __forceinline__ float xsum16(float x) {
   return x + __shfl_xor(x, 32, 64);
 }
 __device__ __forceinline__ int clamp08(int x) { return min(max(x, 0), 8); }
+// Near counts are accumulated as 16-bit integers biased by 2^15 (two per
+// dword, integer LDS atomics: far cheaper here than packed bf16 atomics) and
+// turned into bf16 after they are read.
+constexpr uint32_t kBias2 = 0x80008000u;
+__device__ __forceinline__ void lds_add(unsigned char* p, uint32_t v) {
+  __hip_atomic_fetch_add(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_sub(unsigned char* p, uint32_t v) {
+  __hip_atomic_fetch_sub(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// two biased 16-bit counts -> two bf16 (exact: |count| <= 256); 2^23 + x
+// assembled in the mantissa, then 2^23 + 2^15 subtracted
+__device__ __forceinline__ uint32_t biased_to_bf16x2(uint32_t x) {
+  const float lo = __uint_as_float(0x4B000000u | (x & 0xFFFFu)) - 8421376.0f;
+  const float hi = __uint_as_float(0x4B000000u | (x >> 16)) - 8421376.0f;
+  return pack_bf16(lo, hi);
+}
+// Workgroup barrier that orders LDS only: global loads stay in flight (an
+// LDS DMA still in flight is waited for, as its data lands in LDS).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 __device__ __forceinline__ u32x4 lds128(const unsigned char* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x2 lds_tr16(const unsigned char* p) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(const_cast<unsigned char*>(p)));
@@ -390,12 +408,6 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2)) 
   unsigned char* stage1 = smem + G::STAGE;
   unsigned char* hc = stage1;  // near counts live in stage 1 until the prologue ends
   unsigned char* sm = smem + G::BIG;
-  PlanRec* sRec = reinterpret_cast<PlanRec*>(sm + SM_REC);
-  int* sAa = reinterpret_cast<int*>(sm + SM_AA);
-  int* sAe = reinterpret_cast<int*>(sm + SM_AE);
-  int* sEe = reinterpret_cast<int*>(sm + SM_EE);
-  int* sEa = reinterpret_cast<int*>(sm + SM_EA);
-  int* sSc = reinterpret_cast<int*>(sm + SM_SC);
 
   F f;
   const int tid = threadIdx.x;
@@ -418,16 +430,58 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2)) 
   const int n = A.n, s = A.s;
   const int r0 = qt * BM;
   const int nrows = min(BM, n - r0);
-  const int rlast = r0 + nrows - 1;
   const T* Qp = static_cast<const T*>(A.q) + static_cast<size_t>(b * A.Hq + h) * n * D;
   const T* Kh = static_cast<const T*>(A.k) + static_cast<size_t>(b * A.Hkv + kvh) * n * D;
   const T* Vh = static_cast<const T*>(A.v) + static_cast<size_t>(b * A.Hkv + kvh) * n * D;
   T* Op = static_cast<T*>(A.o) + static_cast<size_t>(b * A.Hq + h) * n * D;
 
-  // first tile (the query rows' own keys) starts loading right away
+  // ---- tile summary and plan bits (issued before the key tiles, so that
+  // waiting for them never waits for a tile)
+  constexpr int SP = 32 * NCH;                 // slots per sorted array
+  int va0 = INT_MAX, va1 = INT_MAX;            // a_i sorted (lane k: k-th, k+64-th)
+  int ve0 = INT_MIN, ve1 = INT_MIN;            // e2_i sorted descending
+  u32x4 aeL[PL ? NCH : 1][2];                  // e_i of slots 32 ch + 8 g .. + 7 (a order)
+  u32x4 eaL[(PL && !CAUSAL) ? NCH : 1][2];     // a2_i of those slots (e2 order)
+  u32x4 pb[2];                                 // plan bits of hashes lane, lane + 64
+  int lo = 0, hi = n, afull = INT_MAX, efull = INT_MIN, cntA = 0;
+  if constexpr (PL) {
+    const size_t tix = static_cast<size_t>(h) * A.ntile + qt;
+    const int* mt = A.meta + tix * A.mstride;
+    const PlanRec* rec = A.plan + tix * s;
+    lo = __builtin_amdgcn_readfirstlane(mt[META_LO]);
+    hi = __builtin_amdgcn_readfirstlane(mt[META_HI]);
+    afull = __builtin_amdgcn_readfirstlane(mt[META_AFULL]);
+    efull = __builtin_amdgcn_readfirstlane(mt[META_EFULL]);
+    cntA = __builtin_amdgcn_readfirstlane(mt[META_CNTA]);
+    const int* aa = mt + META_HDR;
+    va0 = aa[lane];
+    if constexpr (NCH == 4) va1 = aa[64 + lane];
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+      for (int x = 0; x < 2; ++x) aeL[ch][x] = *reinterpret_cast<const u32x4*>(aa + SP + 32 * ch + 8 * g + 4 * x);
+    if constexpr (!CAUSAL) {
+      ve0 = aa[2 * SP + lane];
+      if constexpr (NCH == 4) ve1 = aa[2 * SP + 64 + lane];
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+          eaL[ch][x] = *reinterpret_cast<const u32x4*>(aa + 3 * SP + 32 * ch + 8 * g + 4 * x);
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int i = lane + 64 * x;
+      pb[x] = (x == 0 || NCH == 4) && i < s ? *reinterpret_cast<const u32x4*>(rec[i < s ? i : 0].bits)
+                                            : u32x4{0, 0, 0, 0};
+    }
+  }
+
+  // first tile (the query rows' own keys): loaded right away, or (PLSH)
+  // right after the first barrier of the count set-up, which would wait for it
   TileLoader<D, BF> ld;
   ld.init(w, lane);
-  ld.issue(Kh, Vh, r0, n, stage0, w);
+  if constexpr (!PL) ld.issue(Kh, Vh, r0, n, stage0, w);
 
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
@@ -456,94 +510,64 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2)) 
   }
   f.init_offsets();
 
-  // ---- window of keys that can carry weight; count operands
-  int lo, hi, afull = INT_MAX, efull = INT_MIN, cntA = 0;
+  // ---- count operands
   u32x4 hf[2][4];                          // near: H (operand B) per position chunk
   u32x4 ufl[2][PL ? NCH : 1];              // left:  [r < e_slot]
   u32x4 ufr[2][(PL && !CAUSAL) ? NCH : 1]; // right: [r >= a2_slot]
-  int va0 = INT_MAX, va1 = INT_MAX;        // sorted a_i (lane k: k-th, k-64-th)
-  int ve0 = INT_MIN, ve1 = INT_MIN;        // e2_i sorted descending
   if constexpr (PL) {
-    // zero the near-count matrix (stage 1, not yet in use)
-    for (int x = tid; x < G::HC / 16; x += NT) reinterpret_cast<u32x4*>(hc)[x] = u32x4{0, 0, 0, 0};
-    if (tid < s) sRec[tid] = A.plan[(static_cast<size_t>(h) * A.ntile + qt) * s + tid];
+    // clear the near-count matrix (stage 1, not yet in use; row 128 is spare)
+    for (int x = tid; x < G::HC / 16; x += NT) reinterpret_cast<u32x4*>(hc)[x] = u32x4{kBias2, kBias2, kBias2, kBias2};
     if (tid < 9) {
       u32x4 p;
 #pragma unroll
       for (int q = 0; q < 4; ++q) p[q] = (tid >= 2 * q + 2) ? 0x3F803F80u : (tid == 2 * q + 1 ? 0x00003F80u : 0u);
       *reinterpret_cast<u32x4*>(sm + SM_TH + 16 * tid) = p;
     }
-    __syncthreads();
-    if (w < 2) {
-      // near counts: thread p owns row r0 + p (column p of the [position][row] matrix)
-      const int p = tid, wp = p >> 5, bp = p & 31;
-      for (int i = 0; i < s; ++i) {
-        const u32x4 bw = *reinterpret_cast<const u32x4*>(sRec[i].bits);
-        int st = 0, en = BM;
+    lds_barrier();
+    ld.issue(Kh, Vh, r0, n, stage0, w);
+    {
+      // H[r][p] (stored [p][r], biased int16) by atomic adds: wave w takes the
+      // rows 64 (w & 1) + lane and the hashes of parity w >> 1.  For row r and
+      // hash i, +1 at the start of the block of r (0 when it starts before
+      // the tile) and -1 at its end (the spare row 128 when past the tile).
+      // The boundary bits are wave-uniform, so every branch here is scalar.
+      const int up = w & 1, par = w >> 1;
+      const uint64_t le = lane == 63 ? ~0ull : ((2ull << lane) - 1);  // bits <= lane
+      unsigned char* col = hc + 2 * (64 * up + lane - (lane & 1));
+      const uint32_t onev = 1u << (16 * (lane & 1));
+      int nfull = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t le = q < wp ? 0xFFFFFFFFu : (q == wp ? (0xFFFFFFFFu >> (31 - bp)) : 0u);
-          const uint32_t m = bw[q] & le;
-          st = m ? 32 * q + 31 - __builtin_clz(m) : st;
-        }
-#pragma unroll
-        for (int q = 3; q >= 0; --q) {
-          const uint32_t gt = q > wp ? 0xFFFFFFFFu : (q == wp ? (bp == 31 ? 0u : (0xFFFFFFFEu << bp)) : 0u);
-          const uint32_t m = bw[q] & gt;
-          en = m ? 32 * q + __builtin_ctz(m) : en;
-        }
-        uint16_t* cs = reinterpret_cast<uint16_t*>(hc + st * (2 * BM) + 2 * p);
-        *cs = static_cast<uint16_t>(__float_as_uint(__uint_as_float(static_cast<uint32_t>(*cs) << 16) + 1.0f) >> 16);
-        if (en < BM) {
-          uint16_t* ce = reinterpret_cast<uint16_t*>(hc + en * (2 * BM) + 2 * p);
-          *ce = static_cast<uint16_t>(__float_as_uint(__uint_as_float(static_cast<uint32_t>(*ce) << 16) - 1.0f) >> 16);
-        }
-      }
-    } else {
-      // ranks of the hashes by a (wave 2) and by e2 descending (wave 3)
-      for (int i = lane; i < s; i += 64) {
-        const PlanRec me = sRec[i];
-        int rk = 0;
-        if (w == 2) {
-          for (int k2 = 0; k2 < s; ++k2) {
-            const int ak = sRec[k2].a;
-            rk += (ak < me.a) || (ak == me.a && k2 < i);
+      for (int x = 0; x < 2; ++x) {
+        if (x == 1 && NCH != 4) break;
+        const int iend = min(s, 64 * x + 64);
+        for (int i = 64 * x + par; i < iend; i += 2) {
+          const uint32_t b0 = __builtin_amdgcn_readlane(pb[x][0], i & 63);
+          const uint32_t b1 = __builtin_amdgcn_readlane(pb[x][1], i & 63);
+          const uint32_t b2 = __builtin_amdgcn_readlane(pb[x][2], i & 63);
+          const uint32_t b3 = __builtin_amdgcn_readlane(pb[x][3], i & 63);
+          const uint64_t lo64 = b0 | (static_cast<uint64_t>(b1) << 32);
+          const uint64_t hi64 = b2 | (static_cast<uint64_t>(b3) << 32);
+          if ((lo64 | hi64) == 0) {  // one block over the whole tile
+            ++nfull;
+            continue;
           }
-          sAa[rk] = me.a;
-          sAe[rk] = me.e;
-        } else {
-          for (int k2 = 0; k2 < s; ++k2) {
-            const int ek = sRec[k2].e2;
-            rk += (ek > me.e2) || (ek == me.e2 && k2 < i);
+          const uint64_t W = up ? hi64 : lo64;
+          int st0 = 0, en0 = BM;  // when the row's own half holds no boundary
+          if (up) {
+            if (lo64) st0 = 63 - __builtin_clzll(lo64);
+          } else {
+            if (hi64) en0 = 64 + __builtin_ctzll(hi64);
           }
-          sEe[rk] = me.e2;
-          sEa[rk] = me.a2;
+          const uint64_t m = W & le, gt = W & ~le;
+          const int st = m ? 64 * up + 63 - __builtin_clzll(m) : st0;
+          const int en = gt ? 64 * up + __builtin_ctzll(gt) : en0;
+          lds_add(col + st * (2 * BM), onev);
+          lds_sub(col + en * (2 * BM), onev);
         }
       }
-      if (w == 2) {
-        int vlo = INT_MAX, vhi = INT_MIN, vaf = INT_MAX, vef = INT_MIN, vca = 0;
-        for (int i = lane; i < s; i += 64) {
-          const PlanRec& Rr = sRec[i];
-          vlo = min(vlo, Rr.a);
-          vhi = max(vhi, Rr.e2);
-          if (Rr.e > rlast) vaf = min(vaf, Rr.a);
-          if (Rr.a2 <= r0) vef = max(vef, Rr.e2);
-          vca += Rr.a < r0;
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          vlo = min(vlo, __shfl_xor(vlo, o, 64));
-          vhi = max(vhi, __shfl_xor(vhi, o, 64));
-          vaf = min(vaf, __shfl_xor(vaf, o, 64));
-          vef = max(vef, __shfl_xor(vef, o, 64));
-          vca += __shfl_xor(vca, o, 64);
-        }
-        if (lane == 0) {
-          sSc[0] = vlo; sSc[1] = vhi; sSc[2] = vaf; sSc[3] = vef; sSc[4] = vca;
-        }
-      }
+      if (nfull > 0) lds_add(col, static_cast<uint32_t>(nfull) * onev);
     }
-    __syncthreads();
+    lds_barrier();
     // H operand through transposing reads of the [position][row] matrix:
     // source lane a + 4t of a 16-lane group reads rows 4a..4a+3 at position p0 + t
 #pragma unroll
@@ -554,38 +578,31 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2)) 
         const unsigned char* base = hc + (p0 + (l16 >> 2)) * (2 * BM) + 2 * (32 * w + 16 * rb + 4 * (l16 & 3));
         const u32x2 x0 = lds_tr16(base);
         const u32x2 x1 = lds_tr16(base + 4 * (2 * BM));
-        hf[rb][ch] = u32x4{x0[0], x0[1], x1[0], x1[1]};
+        hf[rb][ch] = u32x4{biased_to_bf16x2(x0[0]), biased_to_bf16x2(x0[1]), biased_to_bf16x2(x1[0]),
+                           biased_to_bf16x2(x1[1])};
       }
+    // far operands: slot k of the a order counts for row r iff r < e_k; slot
+    // k of the e2 order iff r >= a2_k (sentinel slots never count)
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
-        u32x4 fl = {0, 0, 0, 0}, fr = {0, 0, 0, 0};
+        u32x4 fl, fr;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int slot = 32 * ch + 8 * g + t;
-          const uint32_t one = 0x3F80u << (16 * (t & 1));
-          if (slot < s && f.R[rb] < sAe[slot]) fl[t >> 1] |= one;
-          if (!CAUSAL && slot < s && f.R[rb] >= sEa[slot]) fr[t >> 1] |= one;
+        for (int u2 = 0; u2 < 4; ++u2) {
+          const int e0 = static_cast<int>(aeL[ch][u2 >> 1][2 * (u2 & 1)]);
+          const int e1 = static_cast<int>(aeL[ch][u2 >> 1][2 * (u2 & 1) + 1]);
+          fl[u2] = (f.R[rb] < e0 ? 0x3F80u : 0u) | (f.R[rb] < e1 ? 0x3F800000u : 0u);
+          if constexpr (!CAUSAL) {
+            const int a0 = static_cast<int>(eaL[ch][u2 >> 1][2 * (u2 & 1)]);
+            const int a1 = static_cast<int>(eaL[ch][u2 >> 1][2 * (u2 & 1) + 1]);
+            fr[u2] = (f.R[rb] >= a0 ? 0x3F80u : 0u) | (f.R[rb] >= a1 ? 0x3F800000u : 0u);
+          }
         }
         ufl[rb][ch] = fl;
         if constexpr (!CAUSAL) ufr[rb][ch] = fr;
       }
     }
-    va0 = lane < s ? sAa[lane] : INT_MAX;
-    va1 = lane + 64 < s ? sAa[lane + 64] : INT_MAX;
-    if constexpr (!CAUSAL) {
-      ve0 = lane < s ? sEe[lane] : INT_MIN;
-      ve1 = lane + 64 < s ? sEe[lane + 64] : INT_MIN;
-    }
-    lo = __builtin_amdgcn_readfirstlane(sSc[0]);
-    hi = __builtin_amdgcn_readfirstlane(sSc[1]);
-    afull = __builtin_amdgcn_readfirstlane(sSc[2]);
-    efull = __builtin_amdgcn_readfirstlane(sSc[3]);
-    cntA = __builtin_amdgcn_readfirstlane(sSc[4]);
-  } else {
-    lo = 0;
-    hi = n;
   }
 
   // ---- tile schedule
@@ -782,6 +799,8 @@ hipError_t launch_plsh_fwd(const void* q, const void* k, const void* v, void* o,
   FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.plan = reinterpret_cast<const PlanRec*>(static_cast<const char*>(bins) + L.off_plan);
+  a.meta = reinterpret_cast<const int*>(static_cast<const char*>(bins) + L.off_meta);
+  a.mstride = meta_stride_ints(s);
   a.B = batch; a.Hq = hq; a.Hkv = hkv; a.n = n; a.s = s;
   a.ntile = (n + BM - 1) / BM;
   const int grid = grid_size(a.ntile, batch * hq, &a.cs);
@@ -796,6 +815,8 @@ hipError_t launch_alibi_fwd(const void* q, const void* k, const void* v, void* o
   FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.plan = nullptr;
+  a.meta = nullptr;
+  a.mstride = 0;
   a.B = batch; a.Hq = hq; a.Hkv = hkv; a.n = n; a.s = 1;
   a.ntile = (n + BM - 1) / BM;
   const int grid = grid_size(a.ntile, batch * hq, &a.cs);
