@@ -62,6 +62,8 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+typedef __attribute__((address_space(3))) unsigned char lds_uchar_t;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NT = 256;    // threads per workgroup
 constexpr int NW = 4;      // waves per workgroup
@@ -170,25 +172,37 @@ struct TileLoader {
     }
   }
   // K/V rows j0 .. j0 + 63 into one stage; rows at or past n read as zero.
+  //
+  // The loads are written as inline assembly on purpose: the compiler treats
+  // every later LDS access as possibly aliasing an LDS load in flight and
+  // would wait for it, serialising compute on tile t with the load of tile
+  // t + 1.  The data is consumed only after the full wait of the tile
+  // barrier, which is therefore the one synchronisation these loads need.
   __device__ __forceinline__ void issue(const void* Kh, const void* Vh, int j0, int n, unsigned char* stage,
                                         int w) const {
-#if defined(__HIP_DEVICE_COMPILE__)
-    // (the host compilation pass must not see this builtin: with it, clang
-    // silently omits the host launch stubs of the kernels that inline it)
     const int rows = n - j0;
     const int nrec = rows > 0 ? rows * G::RB : 0;
     const size_t off = static_cast<size_t>(j0) * G::RB;
-    __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(static_cast<const char*>(Kh)) + off, (short)0, nrec, 0x00020000);
-    __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(static_cast<const char*>(Vh)) + off, (short)0, nrec, 0x00020000);
+    const uint64_t kb = reinterpret_cast<uint64_t>(Kh) + off;
+    const uint64_t vb = reinterpret_cast<uint64_t>(Vh) + off;
+    // buffer resources: base, 32-bit data format, num_records = bytes left
+    const i32x4 rk = {static_cast<int>(kb), static_cast<int>((kb >> 32) & 0xFFFF), nrec, 0x00020000};
+    const i32x4 rv = {static_cast<int>(vb), static_cast<int>((vb >> 32) & 0xFFFF), nrec, 0x00020000};
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_uchar_t*)(stage)));
 #pragma unroll
     for (int i = 0; i < G::NI; ++i) {
       const int I = w * G::NI + i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(stage + I * 1024), 16, koff[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(stage + G::TILE + I * 1024), 16, voff[i], 0, 0, 0);
+      // lane L's 16 bytes land at M0 + 16 L; s_nop covers the SGPR and M0
+      // write-to-use hazards, which the compiler does not look for in asm
+      asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                   :
+                   : "v"(koff[i]), "s"(rk), "{m0}"(lds0 + I * 1024)
+                   : "memory");
+      asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                   :
+                   : "v"(voff[i]), "s"(rv), "{m0}"(lds0 + G::TILE + I * 1024)
+                   : "memory");
     }
-#endif
   }
 };
 
