@@ -227,14 +227,14 @@ def copy_calibration(dev, nbytes=1 << 30, reps=5):
     for _ in range(reps):
         b.copy_(a)
     torch.cuda.synchronize()
-    log(f"copy calibration: {reps} copies of {nbytes} bytes")
+    log(f"copy calibration: {reps} copies of {nbytes} bytes = {reps * nbytes} bytes read and written")
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="mistral")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
