@@ -11,8 +11,8 @@
 // computed once per (query, key) pair and weighted by the integer count c,
 // which the matrix cores produce in the layout of S.
 //
-// Work decomposition.  One workgroup (4 waves) owns 128 query rows of one
-// (batch, head); wave w owns rows 32w..32w+31 as two 16-row blocks.  Keys
+// Work decomposition.  One workgroup (NW waves) owns 128 query rows of one
+// (batch, head); wave w owns rows WR w .. WR w + WR - 1 as 16-row blocks.  Keys
 // stream through LDS in 64-key tiles, two stages deep, loaded straight from
 // HBM into LDS by buffer loads (rows past the sequence end read as zero).
 // Order: the two "near" tiles holding the query rows themselves, then tiles
@@ -65,9 +65,11 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 typedef __attribute__((address_space(3))) unsigned char lds_uchar_t;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int NT = 256;    // threads per workgroup
-constexpr int NW = 4;      // waves per workgroup
 constexpr int BM = 128;    // query rows per workgroup
+constexpr int NRB = 1;     // 16-row blocks per wave
+constexpr int WR = 16 * NRB;  // query rows per wave
+constexpr int NW = BM / WR;   // waves per workgroup
+constexpr int NT = 64 * NW;   // threads per workgroup
 constexpr int BN = 64;     // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -93,6 +95,7 @@ struct Geo {
   static constexpr int RPI = 1024 / RB;              // rows per 1 KB load instruction
   static constexpr int TILE = BN * RB;               // bytes of one K or V tile
   static constexpr int NI = TILE / 1024 / NW;        // load instructions per wave per matrix
+  static_assert(TILE % (1024 * NW) == 0, "tile loads split evenly over the waves");
   static constexpr int STAGE = 2 * TILE;             // K tile + V tile
   static constexpr int HC = (BM + 1) * BM * 2;       // near counts, bf16 [p][r], p <= 128
   static constexpr int BIG = 2 * STAGE > STAGE + HC ? 2 * STAGE : STAGE + HC;
@@ -215,12 +218,12 @@ struct Fwd {
 
   // per-lane state
   int lane, l16, g, w;
-  int rr[2], R[2];
+  int rr[NRB], R[NRB];
   float sc, scp, thr, beta;
-  float Mrow[2], Msc[2], lsum[2];
-  f32x4 acc[DB][2];
-  u32x4 qb[2][BF ? KS : 1];
-  float qf[2][BF ? 1 : KS];
+  float Mrow[NRB], Msc[NRB], lsum[NRB];
+  f32x4 acc[DB][NRB];
+  u32x4 qb[NRB][BF ? KS : 1];
+  float qf[NRB][BF ? 1 : KS];
   int koff[BF ? KS : KS / 4];  // logit-operand chunk offsets within a row block
   int vtr[DB];                 // value-operand (transposing read) offsets
   const unsigned char* sTh;
@@ -249,14 +252,14 @@ struct Fwd {
   // ---- one 32-key chunk of a tile: logits, counts, softmax, value product
   template <int KIND>
   __device__ __forceinline__ void chunk(const unsigned char* sK, const unsigned char* sV, int j0, int r0, int n,
-                                        int kc, bool need_mask, const int (&mkey)[4], const u32x4 (&cnt_b)[2][4],
+                                        int kc, bool need_mask, const int (&mkey)[4], const u32x4 (&cnt_b)[NRB][4],
                                         int chmax) {
     const int jc = j0 + 32 * kc;
-    f32x4 sacc[2][2], cacc[2][2];
+    f32x4 sacc[2][NRB], cacc[2][NRB];
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < NRB; ++rb) {
         sacc[x][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
         cacc[x][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
@@ -269,7 +272,7 @@ struct Fwd {
         for (int ks = 0; ks < KS; ++ks) {
           const u32x4 a = lds128(kr + koff[ks]);
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb) sacc[kb2][rb] = mfma_bf16(a, qb[rb][ks], sacc[kb2][rb]);
+          for (int rb = 0; rb < NRB; ++rb) sacc[kb2][rb] = mfma_bf16(a, qb[rb][ks], sacc[kb2][rb]);
         }
       } else {
 #pragma unroll
@@ -278,7 +281,7 @@ struct Fwd {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
+            for (int rb = 0; rb < NRB; ++rb)
               sacc[kb2][rb] = mfma_f32(__uint_as_float(a4[e]), qf[rb][4 * c4 + e], sacc[kb2][rb]);
         }
       }
@@ -296,22 +299,24 @@ struct Fwd {
             if (ch > cm) break;
             const u32x4 th = lds128(sTh + 16 * clamp08(jrel0 + l16 - 32 * ch - 8 * g + 1));
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) cacc[kb2][rb] = mfma_bf16(th, cnt_b[rb][ch], cacc[kb2][rb]);
+            for (int rb = 0; rb < NRB; ++rb) cacc[kb2][rb] = mfma_bf16(th, cnt_b[rb][ch], cacc[kb2][rb]);
           }
         } else {
 #pragma unroll
           for (int ch = 0; ch < NCH; ++ch) {
             const u32x4 th = lds128(sTh + 16 * clamp08(mkey[kb] - 32 * ch - 8 * g));
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) cacc[kb2][rb] = mfma_bf16(th, cnt_b[rb][ch], cacc[kb2][rb]);
+            for (int rb = 0; rb < NRB; ++rb) cacc[kb2][rb] = mfma_bf16(th, cnt_b[rb][ch], cacc[kb2][rb]);
           }
         }
       }
     }
     // weights in log2 units (ALiBi) or logits (PLSH); masking; local maxima
-    float lmx[2] = {-INFINITY, -INFINITY};
+    float lmx[NRB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < NRB; ++rb) lmx[rb] = -INFINITY;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -336,10 +341,12 @@ struct Fwd {
           lmx[rb] = fmaxf(lmx[rb], x);
         }
     // raise the running maximum only when some row outgrows it by the margin
-    const bool grow = lmx[0] > Mrow[0] + thr || lmx[1] > Mrow[1] + thr;
+    bool grow = false;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) grow = grow || lmx[rb] > Mrow[rb] + thr;
     if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < NRB; ++rb) {
         const float mn = fmaxf(Mrow[rb], xmax16(lmx[rb]));
         const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((Mrow[rb] - mn) * scp);
         Mrow[rb] = mn;
@@ -351,9 +358,9 @@ struct Fwd {
     }
     // weights and the value product O^T += V^T P^T
     if constexpr (BF) {
-      u32x4 pf[2];
+      u32x4 pf[NRB];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < NRB; ++rb) {
         float p[2][4];
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
@@ -374,12 +381,12 @@ struct Fwd {
         const u32x2 v1 = lds_tr16(vb + 16 * G::RB + vtr[db]);
         const u32x4 a = {v0[0], v0[1], v1[0], v1[1]};
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) acc[db][rb] = mfma_bf16(a, pf[rb], acc[db][rb]);
+        for (int rb = 0; rb < NRB; ++rb) acc[db][rb] = mfma_bf16(a, pf[rb], acc[db][rb]);
       }
     } else {
-      float p[2][2][4];
+      float p[NRB][2][4];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -400,7 +407,7 @@ struct Fwd {
             const int c = (4 * db + (l16 >> 2)) ^ G::swv(key);
             const float va = *reinterpret_cast<const float*>(vrow + 16 * c);
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) acc[db][rb] = mfma_f32(va, p[rb][kb2][e], acc[db][rb]);
+            for (int rb = 0; rb < NRB; ++rb) acc[db][rb] = mfma_f32(va, p[rb][kb2][e], acc[db][rb]);
           }
         }
     }
@@ -408,7 +415,8 @@ struct Fwd {
 };
 
 template <int D, bool BF, bool CAUSAL, int NCH, int MODE>
-__global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2)) void fwd_kernel(FwdArgs A,
+// second bound: waves per SIMD, from the workgroups that fit a CU's LDS
+__global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) * NW / 4) void fwd_kernel(FwdArgs A,
                                                                                               HeadOrder ord,
                                                                                               HeadScale hsc) {
   using G = Geo<D, BF>;
@@ -498,13 +506,13 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2)) 
   if constexpr (!PL) ld.issue(Kh, Vh, r0, n, stage0, w);
 
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    f.rr[rb] = 32 * w + 16 * rb + l16;
+  for (int rb = 0; rb < NRB; ++rb) {
+    f.rr[rb] = WR * w + 16 * rb + l16;
     f.R[rb] = r0 + f.rr[rb];
   }
   // Q fragments (operand B of S^T = K Q^T)
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < NRB; ++rb) {
     const bool ok = f.R[rb] < n;
     const T* qrow = Qp + static_cast<size_t>(ok ? f.R[rb] : 0) * D;
     if constexpr (BF) {
@@ -525,9 +533,9 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2)) 
   f.init_offsets();
 
   // ---- count operands
-  u32x4 hf[2][4];                          // near: H (operand B) per position chunk
-  u32x4 ufl[2][PL ? NCH : 1];              // left:  [r < e_slot]
-  u32x4 ufr[2][(PL && !CAUSAL) ? NCH : 1]; // right: [r >= a2_slot]
+  u32x4 hf[NRB][4];                          // near: H (operand B) per position chunk
+  u32x4 ufl[NRB][PL ? NCH : 1];              // left:  [r < e_slot]
+  u32x4 ufr[NRB][(PL && !CAUSAL) ? NCH : 1]; // right: [r >= a2_slot]
   if constexpr (PL) {
     // clear the near-count matrix (stage 1, not yet in use; row 128 is spare)
     for (int x = tid; x < G::HC / 16; x += NT) reinterpret_cast<u32x4*>(hc)[x] = u32x4{kBias2, kBias2, kBias2, kBias2};
@@ -541,7 +549,7 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2)) 
     ld.issue(Kh, Vh, r0, n, stage0, w);
     {
       // H[r][p] (stored [p][r], biased int16) by atomic adds: wave w takes the
-      // rows 64 (w & 1) + lane and the hashes of parity w >> 1.  For row r and
+      // rows 64 (w & 1) + lane and the hashes i = w >> 1 mod NW / 2.  For row r and
       // hash i, +1 at the start of the block of r (0 when it starts before
       // the tile) and -1 at its end (the spare row 128 when past the tile).
       // The boundary bits are wave-uniform, so every branch here is scalar.
@@ -554,7 +562,7 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2)) 
       for (int x = 0; x < 2; ++x) {
         if (x == 1 && NCH != 4) break;
         const int iend = min(s, 64 * x + 64);
-        for (int i = 64 * x + par; i < iend; i += 2) {
+        for (int i = 64 * x + par; i < iend; i += NW / 2) {
           const uint32_t b0 = __builtin_amdgcn_readlane(pb[x][0], i & 63);
           const uint32_t b1 = __builtin_amdgcn_readlane(pb[x][1], i & 63);
           const uint32_t b2 = __builtin_amdgcn_readlane(pb[x][2], i & 63);
@@ -585,11 +593,11 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2)) 
     // H operand through transposing reads of the [position][row] matrix:
     // source lane a + 4t of a 16-lane group reads rows 4a..4a+3 at position p0 + t
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
       for (int ch = 0; ch < 4; ++ch) {
         const int p0 = 32 * ch + 8 * g;
-        const unsigned char* base = hc + (p0 + (l16 >> 2)) * (2 * BM) + 2 * (32 * w + 16 * rb + 4 * (l16 & 3));
+        const unsigned char* base = hc + (p0 + (l16 >> 2)) * (2 * BM) + 2 * (WR * w + 16 * rb + 4 * (l16 & 3));
         const u32x2 x0 = lds_tr16(base);
         const u32x2 x1 = lds_tr16(base + 4 * (2 * BM));
         hf[rb][ch] = u32x4{biased_to_bf16x2(x0[0]), biased_to_bf16x2(x0[1]), biased_to_bf16x2(x1[0]),
@@ -598,7 +606,7 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2)) 
     // far operands: slot k of the a order counts for row r iff r < e_k; slot
     // k of the e2 order iff r >= a2_k (sentinel slots never count)
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < NRB; ++rb) {
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
         u32x4 fl, fr;
@@ -635,7 +643,7 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2)) 
   f.thr = 8.0f / f.scp;                            // rescale margin (units of x)
   f.beta = MODE == MODE_ALIBI ? hsc.beta[h] : 0.0f;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < NRB; ++rb) {
     f.Mrow[rb] = -INFINITY;
     f.Msc[rb] = 0.f;
     f.lsum[rb] = 0.f;
@@ -655,22 +663,22 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2)) 
   int t = 0;
   {
     const int mkey0[4] = {0, 0, 0, 0};
-    const int chmax = CAUSAL ? w : 3;
+    const int chmax = CAUSAL ? (WR * w + WR - 1) >> 5 : 3;
     for (; t < nnear; ++t) {
       begin_tile(t);
       const int j0 = tile_j0(t);
       const unsigned char* st = (t & 1) ? stage1 : stage0;
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
-        if (CAUSAL && j0 + 32 * kc > r0 + 32 * w + 31) continue;
+        if (CAUSAL && j0 + 32 * kc > r0 + WR * w + WR - 1) continue;
         f.template chunk<KIND_NEAR>(st, st + G::TILE, j0, r0, n, kc, true, mkey0, hf, chmax);
       }
     }
   }
   {
-    u32x4 cb[2][4];
+    u32x4 cb[NRB][4];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
       for (int ch = 0; ch < 4; ++ch) cb[rb][ch] = PL && ch < NCH ? ufl[rb][ch < NCH ? ch : 0] : u32x4{0, 0, 0, 0};
     int lcnt_hi = cntA;
@@ -704,9 +712,9 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2)) 
     }
   }
   if constexpr (!CAUSAL) {
-    u32x4 cb[2][4];
+    u32x4 cb[NRB][4];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
       for (int ch = 0; ch < 4; ++ch) cb[rb][ch] = PL && ch < NCH ? ufr[rb][ch < NCH ? ch : 0] : u32x4{0, 0, 0, 0};
     int rA = s, rB = s;
@@ -738,7 +746,7 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2)) 
 
   // ---- epilogue: O_r = acc / l
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < NRB; ++rb) {
     const float l = xsum16(f.lsum[rb]);
     const float inv = 1.0f / l;
     if (f.R[rb] >= n) continue;
