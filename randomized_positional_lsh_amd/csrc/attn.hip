@@ -105,9 +105,12 @@ struct Geo {
   __device__ static int swv(int key) { return CPR >= 16 ? 2 * (key & 7) : 2 * (key & 3); }
 };
 
-// small-LDS region: the 9 x 16-byte bf16 prefixes of ones
+// small-LDS region: the 9 x 16-byte bf16 prefixes of ones; per-row support
+// bounds [lo, hi) of the workgroup's rows
 constexpr int SM_TH = 0;
-constexpr int SMALL = 256;
+constexpr int SM_LO = 256;
+constexpr int SM_HI = SM_LO + 4 * BM;
+constexpr int SMALL = SM_HI + 4 * BM;
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -219,6 +222,8 @@ struct Fwd {
   // per-lane state
   int lane, l16, g, w;
   int rr[NRB], R[NRB];
+  int lo_r[NRB], hi_r[NRB];  // support of the row: keys [lo, hi) carry weight (causal cut included)
+  int loF, loL, hiF, hiL;    // wave-uniform: bounds of the wave's first and last row
   float sc, scp, thr, beta;
   float Mrow[NRB], Msc[NRB], lsum[NRB];
   f32x4 acc[DB][NRB];
@@ -252,9 +257,13 @@ struct Fwd {
   // ---- one 32-key chunk of a tile: logits, counts, softmax, value product
   template <int KIND>
   __device__ __forceinline__ void chunk(const unsigned char* sK, const unsigned char* sV, int j0, int r0, int n,
-                                        int kc, bool need_mask, const int (&mkey)[4], const u32x4 (&cnt_b)[NRB][4],
-                                        int chmax) {
+                                        int kc, const int (&mkey)[4], const u32x4 (&cnt_b)[NRB][4], int chmax) {
     const int jc = j0 + 32 * kc;
+    // Row supports are single intervals whose ends grow with the row, so the
+    // chunk misses every row of the wave, lies inside every row's support,
+    // or needs an elementwise mask.
+    if (jc + 32 <= loF || jc >= hiL) return;
+    const bool inside = jc >= loL && jc + 32 <= hiF;
     f32x4 sacc[2][NRB], cacc[2][NRB];
 #pragma unroll
     for (int x = 0; x < 2; ++x)
@@ -324,22 +333,26 @@ struct Fwd {
           const int J = jc + 16 * kb2 + 4 * g + e;
           float x = sacc[kb2][rb][e];
           if constexpr (MODE == MODE_ALIBI) x = fmaf(x, sc, -beta * fabsf(static_cast<float>(R[rb] - J)));
-          bool ok = true;
-          if constexpr (KIND == KIND_NEAR) {
-            if constexpr (PL) ok = cacc[kb2][rb][e] > 0.5f;
-            else ok = J < n;
-            if constexpr (CAUSAL) ok = ok && J <= R[rb];
-            x = ok ? x : -INFINITY;
-          } else {
-            if (need_mask) {
-              if constexpr (PL) ok = cacc[kb2][rb][e] > 0.5f;
-              else ok = J < n;
-              x = ok ? x : -INFINITY;
-            }
-          }
           sacc[kb2][rb][e] = x;
-          lmx[rb] = fmaxf(lmx[rb], x);
         }
+    if (!inside) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int J = jc + 16 * kb2 + 4 * g + e;
+            const bool ok = J >= lo_r[rb] && J < hi_r[rb];
+            sacc[kb2][rb][e] = ok ? sacc[kb2][rb][e] : -INFINITY;
+          }
+    }
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lmx[rb] = fmaxf(lmx[rb], sacc[kb2][rb][e]);
     // raise the running maximum only when some row outgrows it by the margin
     bool grow = false;
 #pragma unroll
@@ -465,15 +478,14 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
   u32x4 aeL[PL ? NCH : 1][2];                  // e_i of slots 32 ch + 8 g .. + 7 (a order)
   u32x4 eaL[(PL && !CAUSAL) ? NCH : 1][2];     // a2_i of those slots (e2 order)
   u32x4 pb[2];                                 // plan bits of hashes lane, lane + 64
-  int lo = 0, hi = n, afull = INT_MAX, efull = INT_MIN, cntA = 0;
+  int pa[2], pe[2];                            // their a (block of the first row) and e2
+  int lo = 0, hi = n, cntA = 0;
   if constexpr (PL) {
     const size_t tix = static_cast<size_t>(h) * A.ntile + qt;
     const int* mt = A.meta + tix * A.mstride;
     const PlanRec* rec = A.plan + tix * s;
     lo = __builtin_amdgcn_readfirstlane(mt[META_LO]);
     hi = __builtin_amdgcn_readfirstlane(mt[META_HI]);
-    afull = __builtin_amdgcn_readfirstlane(mt[META_AFULL]);
-    efull = __builtin_amdgcn_readfirstlane(mt[META_EFULL]);
     cntA = __builtin_amdgcn_readfirstlane(mt[META_CNTA]);
     const int* aa = mt + META_HDR;
     va0 = aa[lane];
@@ -494,8 +506,12 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const int i = lane + 64 * x;
-      pb[x] = (x == 0 || NCH == 4) && i < s ? *reinterpret_cast<const u32x4*>(rec[i < s ? i : 0].bits)
-                                            : u32x4{0, 0, 0, 0};
+      const bool ok = (x == 0 || NCH == 4) && i < s;
+      const PlanRec* ri = rec + (i < s ? i : 0);
+      pb[x] = ok ? *reinterpret_cast<const u32x4*>(ri->bits) : u32x4{0, 0, 0, 0};
+      const u32x4 ae = *reinterpret_cast<const u32x4*>(ri);
+      pa[x] = ok ? static_cast<int>(ae[0]) : INT_MAX;
+      pe[x] = ok ? static_cast<int>(ae[3]) : INT_MIN;
     }
   }
 
@@ -545,6 +561,10 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
       for (int q = 0; q < 4; ++q) p[q] = (tid >= 2 * q + 2) ? 0x3F803F80u : (tid == 2 * q + 1 ? 0x00003F80u : 0u);
       *reinterpret_cast<u32x4*>(sm + SM_TH + 16 * tid) = p;
     }
+    if (tid < BM) {
+      reinterpret_cast<int*>(sm + SM_LO)[tid] = INT_MAX;
+      reinterpret_cast<int*>(sm + SM_HI)[tid] = INT_MIN;
+    }
     lds_barrier();
     ld.issue(Kh, Vh, r0, n, stage0, w);
     {
@@ -553,7 +573,10 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
       // hash i, +1 at the start of the block of r (0 when it starts before
       // the tile) and -1 at its end (the spare row 128 when past the tile).
       // The boundary bits are wave-uniform, so every branch here is scalar.
+      // The same pass gives each row its support [lo, hi): the least block
+      // start and the greatest block end over the hashes.
       const int up = w & 1, par = w >> 1;
+      int lo_acc = INT_MAX, hi_acc = INT_MIN;
       const uint64_t le = lane == 63 ? ~0ull : ((2ull << lane) - 1);  // bits <= lane
       unsigned char* col = hc + 2 * (64 * up + lane - (lane & 1));
       const uint32_t onev = 1u << (16 * (lane & 1));
@@ -567,10 +590,14 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
           const uint32_t b1 = __builtin_amdgcn_readlane(pb[x][1], i & 63);
           const uint32_t b2 = __builtin_amdgcn_readlane(pb[x][2], i & 63);
           const uint32_t b3 = __builtin_amdgcn_readlane(pb[x][3], i & 63);
+          const int ai = __builtin_amdgcn_readlane(pa[x], i & 63);
+          const int ei = __builtin_amdgcn_readlane(pe[x], i & 63);
           const uint64_t lo64 = b0 | (static_cast<uint64_t>(b1) << 32);
           const uint64_t hi64 = b2 | (static_cast<uint64_t>(b3) << 32);
           if ((lo64 | hi64) == 0) {  // one block over the whole tile
             ++nfull;
+            lo_acc = min(lo_acc, ai);
+            hi_acc = max(hi_acc, ei);
             continue;
           }
           const uint64_t W = up ? hi64 : lo64;
@@ -585,9 +612,15 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
           const int en = gt ? 64 * up + __builtin_ctzll(gt) : en0;
           lds_add(col + st * (2 * BM), onev);
           lds_sub(col + en * (2 * BM), onev);
+          lo_acc = min(lo_acc, st ? r0 + st : ai);   // st = 0: the block of row r0
+          hi_acc = max(hi_acc, en < BM ? r0 + en : ei);  // en = BM: the block of the last row
         }
       }
       if (nfull > 0) lds_add(col, static_cast<uint32_t>(nfull) * onev);
+      __hip_atomic_fetch_min(reinterpret_cast<int*>(sm + SM_LO) + 64 * up + lane, lo_acc, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_fetch_max(reinterpret_cast<int*>(sm + SM_HI) + 64 * up + lane, hi_acc, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     lds_barrier();
     // H operand through transposing reads of the [position][row] matrix:
@@ -603,6 +636,12 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
         hf[rb][ch] = u32x4{biased_to_bf16x2(x0[0]), biased_to_bf16x2(x0[1]), biased_to_bf16x2(x1[0]),
                            biased_to_bf16x2(x1[1])};
       }
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      f.lo_r[rb] = reinterpret_cast<const int*>(sm + SM_LO)[f.rr[rb]];
+      f.hi_r[rb] = reinterpret_cast<const int*>(sm + SM_HI)[f.rr[rb]];
+      if constexpr (CAUSAL) f.hi_r[rb] = min(f.hi_r[rb], f.R[rb] + 1);
+    }
     // far operands: slot k of the a order counts for row r iff r < e_k; slot
     // k of the e2 order iff r >= a2_k (sentinel slots never count)
 #pragma unroll
@@ -626,6 +665,18 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
       }
     }
   }
+
+  if constexpr (!PL) {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      f.lo_r[rb] = 0;
+      f.hi_r[rb] = CAUSAL ? min(f.R[rb] + 1, n) : n;
+    }
+  }
+  f.loF = __builtin_amdgcn_readlane(f.lo_r[0], 0);
+  f.hiF = __builtin_amdgcn_readlane(f.hi_r[0], 0);
+  f.loL = __builtin_amdgcn_readlane(f.lo_r[NRB - 1], 15);
+  f.hiL = __builtin_amdgcn_readlane(f.hi_r[NRB - 1], 15);
 
   // ---- tile schedule
   const int nnear = nrows > BN ? 2 : 1;
@@ -669,10 +720,7 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
       const int j0 = tile_j0(t);
       const unsigned char* st = (t & 1) ? stage1 : stage0;
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        if (CAUSAL && j0 + 32 * kc > r0 + WR * w + WR - 1) continue;
-        f.template chunk<KIND_NEAR>(st, st + G::TILE, j0, r0, n, kc, true, mkey0, hf, chmax);
-      }
+      for (int kc = 0; kc < 2; ++kc) f.template chunk<KIND_NEAR>(st, st + G::TILE, j0, r0, n, kc, mkey0, hf, chmax);
     }
   }
   {
@@ -687,7 +735,6 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
       const int j0 = tile_j0(t);
       const unsigned char* st = (t & 1) ? stage1 : stage0;
       int mkey[4] = {0, 0, 0, 0};
-      bool need_mask = false;
       if constexpr (PL) {
         // hashes whose block start a lies in this tile: a in [j0, j0 + 64)
         int clo = lcnt_hi;
@@ -705,10 +752,9 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
           for (int kb = 0; kb < 4; ++kb) mkey[kb] += (j0 + 16 * kb + l16 >= av);
         }
         lcnt_hi = clo;
-        need_mask = j0 < afull;
       }
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) f.template chunk<KIND_LEFT>(st, st + G::TILE, j0, r0, n, kc, need_mask, mkey, cb, 0);
+      for (int kc = 0; kc < 2; ++kc) f.template chunk<KIND_LEFT>(st, st + G::TILE, j0, r0, n, kc, mkey, cb, 0);
     }
   }
   if constexpr (!CAUSAL) {
@@ -723,7 +769,6 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
       const int j0 = tile_j0(t);
       const unsigned char* st = (t & 1) ? stage1 : stage0;
       int mkey[4] = {0, 0, 0, 0};
-      bool need_mask;
       if constexpr (PL) {
         while (rA > 0 && __builtin_amdgcn_readlane(rA - 1 < 64 ? ve0 : ve1, (rA - 1) & 63) < j0 + BN) --rA;
         while (rB > 0 && __builtin_amdgcn_readlane(rB - 1 < 64 ? ve0 : ve1, (rB - 1) & 63) <= j0) --rB;
@@ -734,13 +779,9 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) mkey[kb] += (ev > j0 + 16 * kb + l16);
         }
-        need_mask = j0 + BN > efull;
-      } else {
-        need_mask = j0 + BN > n;
       }
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-        f.template chunk<KIND_RIGHT>(st, st + G::TILE, j0, r0, n, kc, need_mask, mkey, cb, 0);
+      for (int kc = 0; kc < 2; ++kc) f.template chunk<KIND_RIGHT>(st, st + G::TILE, j0, r0, n, kc, mkey, cb, 0);
     }
   }
 
