@@ -224,6 +224,7 @@ struct Fwd {
   int rr[NRB], R[NRB];
   int lo_r[NRB], hi_r[NRB];  // support of the row: keys [lo, hi) carry weight (causal cut included)
   int loF, loL, hiF, hiL;    // wave-uniform: bounds of the wave's first and last row
+  float nbase[NRB][4];       // near counts at the key before each 32-position chunk of the tile
   float sc, scp, thr, beta;
   float Mrow[NRB], Msc[NRB], lsum[NRB];
   f32x4 acc[DB][NRB];
@@ -255,9 +256,10 @@ struct Fwd {
   }
 
   // ---- one 32-key chunk of a tile: logits, counts, softmax, value product
-  template <int KIND>
+  // TI: index of the near tile (its keys start at r0 + 64 TI), 0 otherwise
+  template <int KIND, int TI>
   __device__ __forceinline__ void chunk(const unsigned char* sK, const unsigned char* sV, int j0, int r0, int n,
-                                        int kc, const int (&mkey)[4], const u32x4 (&cnt_b)[NRB][4], int chmax) {
+                                        int kc, const int (&mkey)[4], const u32x4 (&cnt_b)[NRB][4]) {
     const int jc = j0 + 32 * kc;
     // Row supports are single intervals whose ends grow with the row, so the
     // chunk misses every row of the wave, lies inside every row's support,
@@ -301,14 +303,14 @@ struct Fwd {
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         const int kb = 2 * kc + kb2;
         if constexpr (KIND == KIND_NEAR) {
-          const int jrel0 = j0 - r0 + 16 * kb;
-          const int cm = min((jrel0 + 15) >> 5, chmax);
+          // c[r, j] = nbase[r][ch] + sum over positions p of chunk ch with p <= j of H[r, p]
+          const int jrel0 = 64 * TI + 16 * kb;
+          const int ch = jrel0 >> 5;
+          const u32x4 th = lds128(sTh + 16 * clamp08(jrel0 + l16 - 32 * ch - 8 * g + 1));
 #pragma unroll
-          for (int ch = 0; ch < 4; ++ch) {
-            if (ch > cm) break;
-            const u32x4 th = lds128(sTh + 16 * clamp08(jrel0 + l16 - 32 * ch - 8 * g + 1));
-#pragma unroll
-            for (int rb = 0; rb < NRB; ++rb) cacc[kb2][rb] = mfma_bf16(th, cnt_b[rb][ch], cacc[kb2][rb]);
+          for (int rb = 0; rb < NRB; ++rb) {
+            const float b0 = nbase[rb][ch];
+            cacc[kb2][rb] = mfma_bf16(th, cnt_b[rb][ch], f32x4{b0, b0, b0, b0});
           }
         } else {
 #pragma unroll
@@ -635,7 +637,25 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
         const u32x2 x1 = lds_tr16(base + 4 * (2 * BM));
         hf[rb][ch] = u32x4{biased_to_bf16x2(x0[0]), biased_to_bf16x2(x0[1]), biased_to_bf16x2(x1[0]),
                            biased_to_bf16x2(x1[1])};
+        // this lane's 8 positions of chunk ch, then the chunk's sum over the 4 lane groups
+        int cs = -8 * 32768;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          cs += static_cast<int>((x0[q] & 0xFFFFu) + (x0[q] >> 16) + (x1[q] & 0xFFFFu) + (x1[q] >> 16));
+        cs += __shfl_xor(cs, 16, 64);
+        cs += __shfl_xor(cs, 32, 64);
+        f.nbase[rb][ch] = static_cast<float>(cs);  // chunk sum for now; prefix below
       }
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      float run = 0.0f;
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) {
+        const float sum = f.nbase[rb][ch];
+        f.nbase[rb][ch] = run;
+        run += sum;
+      }
+    }
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       f.lo_r[rb] = reinterpret_cast<const int*>(sm + SM_LO)[f.rr[rb]];
@@ -713,15 +733,18 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
   };
   int t = 0;
   {
+    // the near tiles: keys r0 .. r0 + 63 in stage 0, r0 + 64 .. r0 + 127 in stage 1
     const int mkey0[4] = {0, 0, 0, 0};
-    const int chmax = CAUSAL ? (WR * w + WR - 1) >> 5 : 3;
-    for (; t < nnear; ++t) {
-      begin_tile(t);
-      const int j0 = tile_j0(t);
-      const unsigned char* st = (t & 1) ? stage1 : stage0;
+    begin_tile(0);
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) f.template chunk<KIND_NEAR>(st, st + G::TILE, j0, r0, n, kc, mkey0, hf, chmax);
+    for (int kc = 0; kc < 2; ++kc) f.template chunk<KIND_NEAR, 0>(stage0, stage0 + G::TILE, r0, r0, n, kc, mkey0, hf);
+    if (nnear > 1) {
+      begin_tile(1);
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+        f.template chunk<KIND_NEAR, 1>(stage1, stage1 + G::TILE, r0 + BN, r0, n, kc, mkey0, hf);
     }
+    t = nnear;
   }
   {
     u32x4 cb[NRB][4];
@@ -754,7 +777,7 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
         lcnt_hi = clo;
       }
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) f.template chunk<KIND_LEFT>(st, st + G::TILE, j0, r0, n, kc, mkey, cb, 0);
+      for (int kc = 0; kc < 2; ++kc) f.template chunk<KIND_LEFT, 0>(st, st + G::TILE, j0, r0, n, kc, mkey, cb);
     }
   }
   if constexpr (!CAUSAL) {
@@ -781,7 +804,7 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
         }
       }
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) f.template chunk<KIND_RIGHT>(st, st + G::TILE, j0, r0, n, kc, mkey, cb, 0);
+      for (int kc = 0; kc < 2; ++kc) f.template chunk<KIND_RIGHT, 0>(st, st + G::TILE, j0, r0, n, kc, mkey, cb);
     }
   }
 
