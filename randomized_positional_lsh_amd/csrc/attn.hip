@@ -157,6 +157,14 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 __device__ __forceinline__ u32x4 lds128(const unsigned char* p) { return *reinterpret_cast<const u32x4*>(p); }
+// 32-bit LDS address of a pointer into the workgroup's LDS, and back
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_uchar_t*)(p)));
+}
+__device__ __forceinline__ u32x2 lds_tr16_at(uint32_t a) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(static_cast<uintptr_t>(a)));
+  return __builtin_bit_cast(u32x2, v);
+}
 __device__ __forceinline__ u32x2 lds_tr16(const unsigned char* p) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(const_cast<unsigned char*>(p)));
   return __builtin_bit_cast(u32x2, v);
@@ -231,7 +239,7 @@ struct Fwd {
   u32x4 qb[NRB][BF ? KS : 1];
   float qf[NRB][BF ? 1 : KS];
   int koff[BF ? KS : KS / 4];  // logit-operand chunk offsets within a row block
-  int vtr[DB];                 // value-operand (transposing read) offsets
+  int vtr0;                    // value-operand (transposing read) offset of block 0; block db: ^ 32 db
   const unsigned char* sTh;
 
   __device__ __forceinline__ void init_offsets() {
@@ -247,11 +255,12 @@ struct Fwd {
     if constexpr (BF) {
       const int a = l16 & 3, t = l16 >> 2;
       const int key = 4 * g + t;  // + 32 kc + 16 hh: multiples of 8, swizzle unchanged
-#pragma unroll
-      for (int db = 0; db < DB; ++db) vtr[db] = key * G::RB + 16 * ((2 * db + (a >> 1)) ^ G::swv(key)) + 8 * (a & 1);
+      // bits: key * RB | 32 (db ^ swv(key) / 2) | 16 (a >> 1) | 8 (a & 1), disjoint fields,
+      // so block db's offset is vtr0 ^ 32 db (stage and chunk bases are multiples of 256)
+      vtr0 = key * G::RB + 16 * ((a >> 1) ^ G::swv(key)) + 8 * (a & 1);
+      static_assert(G::RB % 256 == 0 || G::RB == 128, "V row layout");
     } else {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) vtr[db] = 0;
+      vtr0 = 0;
     }
   }
 
@@ -392,8 +401,9 @@ struct Fwd {
       const unsigned char* vb = sV + (32 * kc) * G::RB;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const u32x2 v0 = lds_tr16(vb + vtr[db]);
-        const u32x2 v1 = lds_tr16(vb + 16 * G::RB + vtr[db]);
+        const uint32_t va = (lds_addr(vb) + vtr0) ^ (32 * db);
+        const u32x2 v0 = lds_tr16_at(va);
+        const u32x2 v1 = lds_tr16_at(va + 16 * G::RB);
         const u32x4 a = {v0[0], v0[1], v1[0], v1[1]};
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) acc[db][rb] = mfma_bf16(a, pf[rb], acc[db][rb]);
