@@ -1,4 +1,4 @@
-// Bin-boundary kernel: from the hashes (delta, u) to the blocks they cut the
+// Bin-boundary kernels: from the hashes (delta, u) to the blocks they cut the
 // positions into.
 //
 // Positional LSH (explainer of arXiv 2605.09472, Methodology 1): random
@@ -11,13 +11,10 @@
 //
 // Bit-exactness: every bin value is floor of the IEEE binary64 quotient of
 // the binary64 difference (x - u) by delta, as in the definition; this file
-// is compiled with -ffp-contract=off.  Two ways to find the starts:
-//  * delta >= 2: consecutive positions differ by at most one bin (the
-//    quotients differ by about 1/delta <= 1/2), so every bin value between
-//    bin(0) and bin(n-1) is met and block k starts at the least x whose bin
-//    is >= bin(0) + k.  That x is found from the estimate ceil(u + K delta)
-//    and corrected with exact bin evaluations (bin is non-decreasing in x).
-//  * delta < 2: evaluate every position and compare with its predecessor.
+// is compiled with -ffp-contract=off.  Each position is evaluated (a product
+// with the reciprocal settles the floor unless the quotient is within a few
+// ulp of an integer, where the division itself is taken) and compared with
+// its predecessor.
 #include <climits>
 
 #include "internal.h"
@@ -25,11 +22,21 @@
 namespace plpsh {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
-__device__ __forceinline__ double bin_at(int x, double u, double delta) {
-  return floor((static_cast<double>(x) - u) / delta);
+// floor((x - u) / delta) for one position, evaluated in binary64: first from
+// the product with a rounded reciprocal, which is within 2.2 ulp of the
+// quotient; when no integer lies within 2^-50 |q| of it the floor is the same
+// as that of the correctly rounded quotient, else the division decides.
+__device__ __forceinline__ double bin_fast(int x, double u, double delta, double rinv) {
+  const double d = static_cast<double>(x) - u;
+  const double q = d * rinv;
+  const double f = floor(q);
+  const double fr = q - f;  // exact for |q| < 2^52
+  const double margin = fabs(q) * 0x1p-50;
+  if (fr > margin && fr < 1.0 - margin) return f;
+  return floor(d / delta);
 }
 
 // Exclusive scan of one int per thread over the workgroup.
@@ -43,19 +50,13 @@ __device__ int wg_exclusive_scan(int v, int* wsum, int* total) {
   }
   if (lane == 63) wsum[w] = x;
   __syncthreads();
-  if (w == 0) {
-    int t = lane < kWaves ? wsum[lane] : 0;
+  int base = 0;
 #pragma unroll
-    for (int o = 1; o < kWaves; o <<= 1) {
-      const int y = __shfl_up(t, o, 64);
-      if (lane >= o) t += y;
-    }
-    if (lane < kWaves) wsum[lane] = t;
-  }
-  __syncthreads();
-  const int base = w ? wsum[w - 1] : 0;
-  *total = wsum[kWaves - 1];
-  __syncthreads();
+  for (int k = 0; k < kWaves; ++k) base += k < w ? wsum[k] : 0;
+  int tot = 0;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) tot += wsum[k];
+  *total = tot;
   return base + x - v;
 }
 
@@ -73,37 +74,24 @@ __global__ __launch_bounds__(kThreads) void bins_kernel(const double* __restrict
   const int h = hid / s, i = hid - h * s;
   const int tid = threadIdx.x;
   const double delta = du[2 * hid], u = du[2 * hid + 1];
+  const double rinv = 1.0 / delta;
 
-  for (int w = tid; w < nwords; w += kThreads) bits[w] = 0u;
-  __syncthreads();
-
-  if (delta >= 2.0) {
-    const double kmin = bin_at(0, u, delta);
-    const double kmax = bin_at(n - 1, u, delta);
-    const int nb = static_cast<int>(kmax - kmin) + 1;
-    for (int k = tid + 1; k < nb; k += kThreads) {
-      const double K = kmin + static_cast<double>(k);
-      const double cand = ceil(u + K * delta);
-      int c = cand < 1.0 ? 1 : (cand > static_cast<double>(n - 1) ? n - 1 : static_cast<int>(cand));
-      // bin(c-1) < K <= bin(c); both loops move at most a step or two
-      for (int it = 0; it < 64 && c > 1 && bin_at(c - 1, u, delta) >= K; ++it) --c;
-      for (int it = 0; it < 64 && c < n - 1 && bin_at(c, u, delta) < K; ++it) ++c;
-      atomicOr(&bits[c >> 5], 1u << (c & 31));
-    }
-    if (tid == 0) atomicOr(&bits[0], 1u);
-  } else {
-    const int lane = tid & 63;
-    for (int x0 = 0; x0 < n; x0 += kThreads) {
-      const int x = x0 + tid;
-      bool f = false;
-      if (x < n) f = (x == 0) || (bin_at(x, u, delta) != bin_at(x - 1, u, delta));
-      const unsigned long long m = __ballot(f);
-      const int xw = x0 + (tid & ~63);  // multiple of 64: two whole words
-      if (lane == 0 && xw < n) {
-        bits[xw >> 5] = static_cast<uint32_t>(m);
-        bits[(xw >> 5) + 1] = static_cast<uint32_t>(m >> 32);
+  // block starts: bit x of the map is set iff x = 0 or bin(x) != bin(x - 1)
+  // (one 32-position word per thread and step; words past n stay zero)
+  const int nused = (n + 31) >> 5;
+  for (int w = tid; w < nwords; w += kThreads) {
+    uint32_t m = 0u;
+    if (w < nused) {
+      const int x0 = 32 * w;
+      double prev = x0 > 0 ? bin_fast(x0 - 1, u, delta, rinv) : -INFINITY;
+      const int cnt = min(32, n - x0);
+      for (int b = 0; b < cnt; ++b) {
+        const double bb = bin_fast(x0 + b, u, delta, rinv);
+        m |= static_cast<uint32_t>(bb != prev) << b;
+        prev = bb;
       }
     }
+    bits[w] = m;
   }
   __syncthreads();
 
@@ -121,12 +109,20 @@ __global__ __launch_bounds__(kThreads) void bins_kernel(const double* __restrict
   __syncthreads();
 
   int32_t* st = starts + static_cast<size_t>(hid) * (n + 1);
-  for (int w = tid; w < nwords; w += kThreads) {
-    uint32_t m = bits[w];
-    int b = pre[w];
-    while (m) {
-      st[b++] = (w << 5) + (__ffs(m) - 1);
-      m &= m - 1;
+  if (delta < 4.0) {
+    // dense: one position per thread, consecutive threads write consecutive starts
+    for (int x = tid; x < n; x += kThreads) {
+      const uint32_t m = bits[x >> 5];
+      if ((m >> (x & 31)) & 1u) st[pre[x >> 5] + __popc(m & ((1u << (x & 31)) - 1u))] = x;
+    }
+  } else {
+    for (int w = tid; w < nused; w += kThreads) {
+      uint32_t m = bits[w];
+      int b = pre[w];
+      while (m) {
+        st[b++] = (w << 5) + (__ffs(m) - 1);
+        m &= m - 1;
+      }
     }
   }
   if (tid == 0) {
@@ -159,7 +155,6 @@ __global__ __launch_bounds__(kThreads) void bins_kernel(const double* __restrict
     pl[static_cast<size_t>(q) * s] = rec;
   }
 }
-
 
 // Tile summaries: one wave per (head, query tile) merges the s plan records
 // of that tile.  The attention kernel takes from here the window of keys that
