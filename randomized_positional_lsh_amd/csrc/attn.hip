@@ -76,7 +76,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 enum { MODE_PLSH = 0, MODE_ALIBI = 1 };
 enum { KIND_NEAR = 0, KIND_LEFT = 1, KIND_RIGHT = 2 };
 
-struct HeadOrder { uint16_t h[1024]; };  // heads, most expensive first
+// heads, most expensive first, two 16-bit entries per word (dword elements
+// keep the lookup a scalar load)
+struct HeadOrder {
+  uint32_t w[512];
+  __host__ __device__ int get(int i) const { return static_cast<int>((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu); }
+  void set(int i, int h) { w[i >> 1] |= static_cast<uint32_t>(h) << (16 * (i & 1)); }
+};
 struct HeadScale { float beta[256]; };   // log2(e) / sigma_h (dense ALiBi)
 
 struct FwdArgs {
@@ -472,7 +478,7 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
   const int qt = xcd * A.cs + kk % A.cs;
   if (qt >= A.ntile) return;
   const int b = inst % A.B;
-  const int h = ord.h[inst / A.B];
+  const int h = ord.get(inst / A.B);
   const int kvh = h / (A.Hq / A.Hkv);
   const int n = A.n, s = A.s;
   const int r0 = qt * BM;
@@ -900,8 +906,8 @@ hipError_t launch_plsh_fwd(const void* q, const void* k, const void* v, void* o,
   a.B = batch; a.Hq = hq; a.Hkv = hkv; a.n = n; a.s = s;
   a.ntile = (n + BM - 1) / BM;
   const int grid = grid_size(a.ntile, batch * hq, &a.cs);
-  HeadOrder ord;
-  for (int i = 0; i < hq; ++i) ord.h[i] = order[i];
+  HeadOrder ord{};
+  for (int i = 0; i < hq; ++i) ord.set(i, order[i]);
   HeadScale hs{};
   return dispatch<MODE_PLSH>(a, ord, hs, d, dtype, causal, grid, st);
 }
@@ -916,8 +922,8 @@ hipError_t launch_alibi_fwd(const void* q, const void* k, const void* v, void* o
   a.B = batch; a.Hq = hq; a.Hkv = hkv; a.n = n; a.s = 1;
   a.ntile = (n + BM - 1) / BM;
   const int grid = grid_size(a.ntile, batch * hq, &a.cs);
-  HeadOrder ord;
-  for (int i = 0; i < hq; ++i) ord.h[i] = static_cast<uint16_t>(i);
+  HeadOrder ord{};
+  for (int i = 0; i < hq; ++i) ord.set(i, i);
   HeadScale hs{};
   for (int i = 0; i < hq; ++i) hs.beta[i] = beta[i];
   return dispatch<MODE_ALIBI>(a, ord, hs, d, dtype, causal, grid, st);
