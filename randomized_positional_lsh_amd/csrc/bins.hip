@@ -14,7 +14,7 @@
 // is compiled with -ffp-contract=off.  Each position is evaluated (a product
 // with the reciprocal settles the floor unless the quotient is within a few
 // ulp of an integer, where the division itself is taken) and compared with
-// its predecessor.
+// its predecessor; position 0 always starts a block.
 #include <climits>
 
 #include "internal.h"
@@ -25,18 +25,39 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
-// floor((x - u) / delta) for one position, evaluated in binary64: first from
-// the product with a rounded reciprocal, which is within 2.2 ulp of the
-// quotient; when no integer lies within 2^-50 |q| of it the floor is the same
-// as that of the correctly rounded quotient, else the division decides.
-__device__ __forceinline__ double bin_fast(int x, double u, double delta, double rinv) {
-  const double d = static_cast<double>(x) - u;
-  const double q = d * rinv;
-  const double f = floor(q);
-  const double fr = q - f;  // exact for |q| < 2^52
-  const double margin = fabs(q) * 0x1p-50;
-  if (fr > margin && fr < 1.0 - margin) return f;
-  return floor(d / delta);
+// Start flags of the 32 positions x0 .. x0 + 31 (bit b: bin(x0 + b) differs
+// from bin(x0 + b - 1)), bins evaluated in binary64 as floor((x - u) / delta).
+// First from the product with a rounded reciprocal, which is within 2.2 ulp
+// of the quotient: where no integer lies within 2^-50 |q| of it the floor
+// equals that of the correctly rounded quotient.  If any of the 33 positions
+// misses that margin (rare) the word is redone with the division itself.
+// The fast pass is fully unrolled so that the evaluations overlap.
+__device__ __forceinline__ uint32_t start_flags(int x0, double u, double delta, double rinv) {
+  double f[33];
+  bool exact = false;
+#pragma unroll
+  for (int k = 0; k < 33; ++k) {
+    const double d = static_cast<double>(x0 - 1 + k) - u;
+    const double q = d * rinv;
+    const double fl = floor(q);
+    const double fr = q - fl;  // exact for |q| < 2^52
+    const double margin = fabs(q) * 0x1p-50;
+    f[k] = fl;
+    exact = exact || !(fr > margin && fr < 1.0 - margin);
+  }
+  uint32_t m = 0u;
+  if (!exact) {
+#pragma unroll
+    for (int b = 0; b < 32; ++b) m |= static_cast<uint32_t>(f[b + 1] != f[b]) << b;
+  } else {
+    double prev = floor((static_cast<double>(x0 - 1) - u) / delta);
+    for (int b = 0; b < 32; ++b) {
+      const double bb = floor((static_cast<double>(x0 + b) - u) / delta);
+      m |= static_cast<uint32_t>(bb != prev) << b;
+      prev = bb;
+    }
+  }
+  return m;
 }
 
 // Exclusive scan of one int per thread over the workgroup.
@@ -83,13 +104,9 @@ __global__ __launch_bounds__(kThreads) void bins_kernel(const double* __restrict
     uint32_t m = 0u;
     if (w < nused) {
       const int x0 = 32 * w;
-      double prev = x0 > 0 ? bin_fast(x0 - 1, u, delta, rinv) : -INFINITY;
-      const int cnt = min(32, n - x0);
-      for (int b = 0; b < cnt; ++b) {
-        const double bb = bin_fast(x0 + b, u, delta, rinv);
-        m |= static_cast<uint32_t>(bb != prev) << b;
-        prev = bb;
-      }
+      m = start_flags(x0, u, delta, rinv);
+      if (x0 == 0) m |= 1u;
+      if (n - x0 < 32) m &= (1u << (n - x0)) - 1u;
     }
     bits[w] = m;
   }
@@ -111,6 +128,7 @@ __global__ __launch_bounds__(kThreads) void bins_kernel(const double* __restrict
   int32_t* st = starts + static_cast<size_t>(hid) * (n + 1);
   if (delta < 4.0) {
     // dense: one position per thread, consecutive threads write consecutive starts
+#pragma unroll 4
     for (int x = tid; x < n; x += kThreads) {
       const uint32_t m = bits[x >> 5];
       if ((m >> (x & 31)) & 1u) st[pre[x >> 5] + __popc(m & ((1u << (x & 31)) - 1u))] = x;
