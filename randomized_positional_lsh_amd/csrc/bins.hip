@@ -130,8 +130,9 @@ __global__ __launch_bounds__(kThreads) void bins_kernel(const double* __restrict
     // dense: one position per thread, consecutive threads write consecutive starts
 #pragma unroll 4
     for (int x = tid; x < n; x += kThreads) {
-      const uint32_t m = bits[x >> 5];
-      if ((m >> (x & 31)) & 1u) st[pre[x >> 5] + __popc(m & ((1u << (x & 31)) - 1u))] = x;
+      const uint32_t m = bits[x >> 5];  // both reads unconditional, so unrolled steps overlap
+      const int o = pre[x >> 5] + __popc(m & ((1u << (x & 31)) - 1u));
+      if ((m >> (x & 31)) & 1u) st[o] = x;
     }
   } else {
     for (int w = tid; w < nused; w += kThreads) {
@@ -168,7 +169,8 @@ __global__ __launch_bounds__(kThreads) void bins_kernel(const double* __restrict
     rec.bits[0] &= ~1u;
     if (n - r0 < kPlanTile) {
       const int p = n - r0;
-      rec.bits[p >> 5] |= 1u << (p & 31);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rec.bits[j] |= (p >> 5) == j ? 1u << (p & 31) : 0u;
     }
     pl[static_cast<size_t>(q) * s] = rec;
   }
