@@ -544,23 +544,21 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
     f.rr[rb] = WR * w + 16 * rb + l16;
     f.R[rb] = r0 + f.rr[rb];
   }
-  // Q fragments (operand B of S^T = K Q^T)
+  // Q fragments (operand B of S^T = K Q^T).  Rows past n read row n - 1: their
+  // results are never stored and rows do not mix, and an unconditional load
+  // is waited for only where it is first used.
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
-    const bool ok = f.R[rb] < n;
-    const T* qrow = Qp + static_cast<size_t>(ok ? f.R[rb] : 0) * D;
+    const T* qrow = Qp + static_cast<size_t>(min(f.R[rb], n - 1)) * D;
     if constexpr (BF) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
-        f.qb[rb][ks] = ok ? x : u32x4{0, 0, 0, 0};
-      }
+      for (int ks = 0; ks < KS; ++ks) f.qb[rb][ks] = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
     } else {
 #pragma unroll
       for (int c4 = 0; c4 < KS / 4; ++c4) {
         const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + KS * g + 4 * c4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) f.qf[rb][4 * c4 + e] = ok ? __uint_as_float(x[e]) : 0.0f;
+        for (int e = 0; e < 4; ++e) f.qf[rb][4 * c4 + e] = __uint_as_float(x[e]);
       }
     }
   }
@@ -587,23 +585,23 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
     ld.issue(Kh, Vh, r0, n, stage0, w);
     {
       // H[r][p] (stored [p][r], biased int16) by atomic adds: wave w takes the
-      // rows 64 (w & 1) + lane and the hashes i = w >> 1 mod NW / 2.  For row r and
-      // hash i, +1 at the start of the block of r (0 when it starts before
-      // the tile) and -1 at its end (the spare row 128 when past the tile).
-      // The boundary bits are wave-uniform, so every branch here is scalar.
-      // The same pass gives each row its support [lo, hi): the least block
-      // start and the greatest block end over the hashes.
-      const int up = w & 1, par = w >> 1;
-      int lo_acc = INT_MAX, hi_acc = INT_MIN;
+      // hashes i = w mod NW for all 128 rows, rows lane and 64 + lane.  For
+      // row r and hash i, +1 at the start of the block of r (0 when it starts
+      // before the tile) and -1 at its end (the spare row 128 when past the
+      // tile).  The boundary bits are wave-uniform, so every branch here is
+      // scalar.  The same pass gives each row its support [lo, hi): the least
+      // block start and the greatest block end over the hashes.
       const uint64_t le = lane == 63 ? ~0ull : ((2ull << lane) - 1);  // bits <= lane
-      unsigned char* col = hc + 2 * (64 * up + lane - (lane & 1));
+      unsigned char* col0 = hc + 2 * (lane - (lane & 1));
+      unsigned char* col1 = col0 + 2 * 64;
       const uint32_t onev = 1u << (16 * (lane & 1));
-      int nfull = 0;
+      int lo0 = INT_MAX, hi0 = INT_MIN, lo1 = INT_MAX, hi1 = INT_MIN;
+      int nfull = 0, flo = INT_MAX, fhi = INT_MIN;  // hashes with one block over the tile
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         if (x == 1 && NCH != 4) break;
         const int iend = min(s, 64 * x + 64);
-        for (int i = 64 * x + par; i < iend; i += NW / 2) {
+        for (int i = 64 * x + w; i < iend; i += NW) {
           const uint32_t b0 = __builtin_amdgcn_readlane(pb[x][0], i & 63);
           const uint32_t b1 = __builtin_amdgcn_readlane(pb[x][1], i & 63);
           const uint32_t b2 = __builtin_amdgcn_readlane(pb[x][2], i & 63);
@@ -614,31 +612,42 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
           const uint64_t hi64 = b2 | (static_cast<uint64_t>(b3) << 32);
           if ((lo64 | hi64) == 0) {  // one block over the whole tile
             ++nfull;
-            lo_acc = min(lo_acc, ai);
-            hi_acc = max(hi_acc, ei);
+            flo = min(flo, ai);
+            fhi = max(fhi, ei);
             continue;
           }
-          const uint64_t W = up ? hi64 : lo64;
-          int st0 = 0, en0 = BM;  // when the row's own half holds no boundary
-          if (up) {
-            if (lo64) st0 = 63 - __builtin_clzll(lo64);
-          } else {
-            if (hi64) en0 = 64 + __builtin_ctzll(hi64);
-          }
-          const uint64_t m = W & le, gt = W & ~le;
-          const int st = m ? 64 * up + 63 - __builtin_clzll(m) : st0;
-          const int en = gt ? 64 * up + __builtin_ctzll(gt) : en0;
-          lds_add(col + st * (2 * BM), onev);
-          lds_sub(col + en * (2 * BM), onev);
-          lo_acc = min(lo_acc, st ? r0 + st : ai);   // st = 0: the block of row r0
-          hi_acc = max(hi_acc, en < BM ? r0 + en : ei);  // en = BM: the block of the last row
+          // row lane (first half)
+          const uint64_t m0 = lo64 & le, g0 = lo64 & ~le;
+          const int st0 = m0 ? 63 - __builtin_clzll(m0) : 0;
+          const int en0 = g0 ? __builtin_ctzll(g0) : (hi64 ? 64 + __builtin_ctzll(hi64) : BM);
+          // row 64 + lane (second half)
+          const uint64_t m1 = hi64 & le, g1 = hi64 & ~le;
+          const int st1 = m1 ? 127 - __builtin_clzll(m1) : (lo64 ? 63 - __builtin_clzll(lo64) : 0);
+          const int en1 = g1 ? 64 + __builtin_ctzll(g1) : BM;
+          lds_add(col0 + st0 * (2 * BM), onev);
+          lds_sub(col0 + en0 * (2 * BM), onev);
+          lds_add(col1 + st1 * (2 * BM), onev);
+          lds_sub(col1 + en1 * (2 * BM), onev);
+          lo0 = min(lo0, st0 ? r0 + st0 : ai);   // st = 0: the block of row r0
+          hi0 = max(hi0, en0 < BM ? r0 + en0 : ei);  // en = BM: the block of the last row
+          lo1 = min(lo1, st1 ? r0 + st1 : ai);
+          hi1 = max(hi1, en1 < BM ? r0 + en1 : ei);
         }
       }
-      if (nfull > 0) lds_add(col, static_cast<uint32_t>(nfull) * onev);
-      __hip_atomic_fetch_min(reinterpret_cast<int*>(sm + SM_LO) + 64 * up + lane, lo_acc, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_WORKGROUP);
-      __hip_atomic_fetch_max(reinterpret_cast<int*>(sm + SM_HI) + 64 * up + lane, hi_acc, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (nfull > 0) {
+        lds_add(col0, static_cast<uint32_t>(nfull) * onev);
+        lds_add(col1, static_cast<uint32_t>(nfull) * onev);
+      }
+      lo0 = min(lo0, flo);
+      lo1 = min(lo1, flo);
+      hi0 = max(hi0, fhi);
+      hi1 = max(hi1, fhi);
+      int* sLo = reinterpret_cast<int*>(sm + SM_LO);
+      int* sHi = reinterpret_cast<int*>(sm + SM_HI);
+      __hip_atomic_fetch_min(sLo + lane, lo0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_fetch_max(sHi + lane, hi0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_fetch_min(sLo + 64 + lane, lo1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_fetch_max(sHi + 64 + lane, hi1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     lds_barrier();
     // H operand through transposing reads of the [position][row] matrix:
