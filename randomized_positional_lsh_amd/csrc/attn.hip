@@ -167,6 +167,9 @@ __device__ __forceinline__ u32x4 lds128(const unsigned char* p) { return *reinte
 __device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_uchar_t*)(p)));
 }
+__device__ __forceinline__ u32x4 lds128_at(uint32_t a) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(static_cast<uintptr_t>(a));
+}
 __device__ __forceinline__ u32x2 lds_tr16_at(uint32_t a) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(static_cast<uintptr_t>(a)));
   return __builtin_bit_cast(u32x2, v);
@@ -244,15 +247,19 @@ struct Fwd {
   f32x4 acc[DB][NRB];
   u32x4 qb[NRB][BF ? KS : 1];
   float qf[NRB][BF ? 1 : KS];
-  int koff[BF ? KS : KS / 4];  // logit-operand chunk offsets within a row block
+  int koff[BF ? 1 : KS / 4];   // fp32: logit-operand chunk offsets within a row block
+  uint32_t kbase;              // bf16: logit-operand offset of k-step 0; k-step ks: ^ 64 ks
+  uint32_t ka[BF ? KS : 1];    // bf16: LDS addresses of the current tile's logit operand, per k-step
   int vtr0;                    // value-operand (transposing read) offset of block 0; block db: ^ 32 db
   const unsigned char* sTh;
 
   __device__ __forceinline__ void init_offsets() {
     // K operand: key = 16 kb + l16; logical chunk c = 4 ks + g (bf16) or (KS/4) g + c4 (fp32)
     if constexpr (BF) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) koff[ks] = l16 * G::RB + 16 * ((4 * ks + g) ^ G::swk(l16));
+      // l16 RB | 16 ((4 ks + g) ^ swk(l16)): the k-step bits 6-7 enter only
+      // through the XOR, so k-step ks is kbase ^ 64 ks
+      kbase = l16 * G::RB + 16 * (g ^ G::swk(l16));
+      koff[0] = 0;
     } else {
 #pragma unroll
       for (int c4 = 0; c4 < KS / 4; ++c4) koff[c4] = l16 * G::RB + 16 * (((KS / 4) * g + c4) ^ G::swk(l16));
@@ -267,6 +274,16 @@ struct Fwd {
       static_assert(G::RB % 256 == 0 || G::RB == 128, "V row layout");
     } else {
       vtr0 = 0;
+    }
+  }
+
+  // per tile: the logit-operand addresses of its stage (stage bases are
+  // multiples of 256, so adding one commutes with the k-step XOR)
+  __device__ __forceinline__ void begin_k(const unsigned char* sK) {
+    if constexpr (BF) {
+      const uint32_t b = lds_addr(sK) + kbase;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) ka[ks] = b ^ (64 * ks);
     }
   }
 
@@ -296,7 +313,7 @@ struct Fwd {
       if constexpr (BF) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 a = lds128(kr + koff[ks]);
+          const u32x4 a = lds128_at(ka[ks] + (16 * (2 * kc + kb2)) * G::RB);
 #pragma unroll
           for (int rb = 0; rb < NRB; ++rb) sacc[kb2][rb] = mfma_bf16(a, qb[rb][ks], sacc[kb2][rb]);
         }
@@ -761,10 +778,12 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
     // the near tiles: keys r0 .. r0 + 63 in stage 0, r0 + 64 .. r0 + 127 in stage 1
     const int mkey0[4] = {0, 0, 0, 0};
     begin_tile(0);
+    f.begin_k(stage0);
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) f.template chunk<KIND_NEAR, 0>(stage0, stage0 + G::TILE, r0, r0, n, kc, mkey0, hf);
     if (nnear > 1) {
       begin_tile(1);
+      f.begin_k(stage1);
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
         f.template chunk<KIND_NEAR, 1>(stage1, stage1 + G::TILE, r0 + BN, r0, n, kc, mkey0, hf);
@@ -801,6 +820,7 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
         }
         lcnt_hi = clo;
       }
+      f.begin_k(st);
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) f.template chunk<KIND_LEFT, 0>(st, st + G::TILE, j0, r0, n, kc, mkey, cb);
     }
@@ -828,6 +848,7 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
           for (int kb = 0; kb < 4; ++kb) mkey[kb] += (ev > j0 + 16 * kb + l16);
         }
       }
+      f.begin_k(st);
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) f.template chunk<KIND_RIGHT, 0>(st, st + G::TILE, j0, r0, n, kc, mkey, cb);
     }
