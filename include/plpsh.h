@@ -130,18 +130,6 @@ plpsh_status plpsh_draw_hashes(uint64_t seed, int32_t heads, int32_t s,
  *             int32 a2, e2  block containing row min(128 q + 127, n - 1)
  *             uint32 bits[4] bit p set iff position 128 q + p (1 <= p < 128)
  *                            starts a block, or equals n
- *   meta  : int32 [H][T][W], W = 8 + 4 P rounded up to a multiple of 16,
- *           P = 32, 64 or 128 (the least >= s): the plan records of one
- *           query tile merged (rows r0 = 128 q .. rl = min(r0 + 127, n - 1)):
- *             [0] min_i a_i            [1] max_i e2_i
- *             [2] min a_i over hashes with e_i > rl (INT32_MAX if none)
- *             [3] max e2_i over hashes with a2_i <= r0 (INT32_MIN if none)
- *             [4] #{i : a_i < r0}      [5..7] zero
- *             [8      .. 8+P)   a_i sorted ascending (ties: lower i first)
- *             [8+P    .. 8+2P)  e_i in that order
- *             [8+2P   .. 8+3P)  e2_i sorted descending (ties: lower i first)
- *             [8+3P   .. 8+4P)  a2_i in that order
- *           slots s..P-1 hold INT32_MAX, INT32_MIN, INT32_MIN, INT32_MAX.
  *
  * Block k of hash t is the maximal run of positions with equal bin value
  * floor((x - u) / delta) evaluated in IEEE binary64 (Methodology 1: bins of
@@ -150,8 +138,7 @@ plpsh_status plpsh_draw_hashes(uint64_t seed, int32_t heads, int32_t s,
  */
 size_t plpsh_bins_bytes(int32_t heads, int32_t s, int32_t n);
 plpsh_status plpsh_bins_layout(int32_t heads, int32_t s, int32_t n,
-                               size_t* off_nblk, size_t* off_starts, size_t* off_plan,
-                               size_t* off_meta);
+                               size_t* off_nblk, size_t* off_starts, size_t* off_plan);
 
 /*
  * plpsh_sample_bins -- draw hashes on the host (as plpsh_draw_hashes) and,

@@ -15,8 +15,6 @@ from ._binding import (  # noqa: F401
     attention_hashes,
     bins_from_hashes,
     bins_layout,
-    meta_slots,
-    meta_stride,
     draw_hashes,
     raw,
     sample_bins,

@@ -46,7 +46,7 @@ _SIGS = {
     "plpsh_last_hip_error": (ctypes.c_char_p, []),
     "plpsh_draw_hashes": (_c_int, [ctypes.c_uint64, _c_int, _c_int, _dp, _dp, _dp]),
     "plpsh_bins_bytes": (_c_sz, [_c_int, _c_int, _c_int]),
-    "plpsh_bins_layout": (_c_int, [_c_int, _c_int, _c_int, _szp, _szp, _szp, _szp]),
+    "plpsh_bins_layout": (_c_int, [_c_int, _c_int, _c_int, _szp, _szp, _szp]),
     "plpsh_sample_bins": (_c_int, [ctypes.c_uint64, _c_int, _c_int, _c_int, _dp, _dp, _dp, _vp, _c_sz, _vp]),
     "plpsh_bins_from_hashes": (_c_int, [_c_int, _c_int, _c_int, _dp, _dp, _vp, _c_sz, _vp]),
     "plpsh_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int]),
@@ -112,21 +112,10 @@ def draw_hashes(seed: int, sigma, s: int) -> tuple[np.ndarray, np.ndarray]:
 
 
 def bins_layout(heads: int, s: int, n: int) -> dict:
-    a, b, c, d = (ctypes.c_size_t() for _ in range(4))
-    _check(_lib.plpsh_bins_layout(heads, s, n, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c), ctypes.byref(d)),
+    a, b, c = (ctypes.c_size_t() for _ in range(3))
+    _check(_lib.plpsh_bins_layout(heads, s, n, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)),
            "plpsh_bins_layout")
-    return {"nblk": a.value, "starts": b.value, "plan": c.value, "meta": d.value,
-            "total": _lib.plpsh_bins_bytes(heads, s, n)}
-
-
-def meta_slots(s: int) -> int:
-    """Slots per sorted array of a tile summary (32, 64 or 128)."""
-    return 32 if s <= 32 else (64 if s <= 64 else 128)
-
-
-def meta_stride(s: int) -> int:
-    """int32 entries per tile summary."""
-    return (8 + 4 * meta_slots(s) + 15) // 16 * 16
+    return {"nblk": a.value, "starts": b.value, "plan": c.value, "total": _lib.plpsh_bins_bytes(heads, s, n)}
 
 
 def workspace_bytes(heads_q: int, s: int, n: int) -> int:
@@ -162,8 +151,6 @@ class Bins:
         self.starts = b8[L["starts"]:L["starts"] + 4 * hs * (n + 1)].view(torch.int32).view(hs, n + 1)
         ntile = (n + PLAN_TILE - 1) // PLAN_TILE
         self.plan = b8[L["plan"]:L["plan"] + 32 * heads * ntile * s].view(torch.int32).view(heads, ntile, s, 8)
-        W = meta_stride(s)
-        self.meta = b8[L["meta"]:L["meta"] + 4 * heads * ntile * W].view(torch.int32).view(heads, ntile, W)
 
 
 def _bins_buffer(heads, s, n, device):

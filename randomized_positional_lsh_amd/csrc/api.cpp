@@ -190,14 +190,13 @@ size_t plpsh_bins_bytes(int32_t heads, int32_t s, int32_t n) {
 }
 
 plpsh_status plpsh_bins_layout(int32_t heads, int32_t s, int32_t n, size_t* off_nblk, size_t* off_starts,
-                               size_t* off_plan, size_t* off_meta) {
-  if (!valid_hs(heads, s) || n < 1 || n > PLPSH_MAX_N || !off_nblk || !off_starts || !off_plan || !off_meta)
+                               size_t* off_plan) {
+  if (!valid_hs(heads, s) || n < 1 || n > PLPSH_MAX_N || !off_nblk || !off_starts || !off_plan)
     return PLPSH_ERR_INVALID_ARGUMENT;
   const BinsLayout L = plpsh::bins_layout(heads, s, n);
   *off_nblk = L.off_nblk;
   *off_starts = L.off_starts;
   *off_plan = L.off_plan;
-  *off_meta = L.off_meta;
   return PLPSH_OK;
 }
 

@@ -88,8 +88,7 @@ struct HeadScale { float beta[256]; };   // log2(e) / sigma_h (dense ALiBi)
 struct FwdArgs {
   const void* q; const void* k; const void* v; void* o;
   const PlanRec* plan;
-  const int* meta;  // tile summaries, mstride ints each
-  int B, Hq, Hkv, n, s, ntile, cs, mstride;
+  int B, Hq, Hkv, n, s, ntile, cs;
 };
 
 template <int D, bool BF>
@@ -116,7 +115,8 @@ struct Geo {
 constexpr int SM_TH = 0;
 constexpr int SM_LO = 256;
 constexpr int SM_HI = SM_LO + 4 * BM;
-constexpr int SMALL = SM_HI + 4 * BM;
+constexpr int SM_SORT = SM_HI + 4 * BM;      // 4 x 128 ints: a, e in a order; e2, a2 in e2 order
+constexpr int SMALL = SM_SORT + 4 * 4 * 128;
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -505,48 +505,29 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
   const T* Vh = static_cast<const T*>(A.v) + static_cast<size_t>(b * A.Hkv + kvh) * n * D;
   T* Op = static_cast<T*>(A.o) + static_cast<size_t>(b * A.Hq + h) * n * D;
 
-  // ---- tile summary and plan bits (issued before the key tiles, so that
-  // waiting for them never waits for a tile)
+  // ---- plan records of the tile's hashes (issued before the key tiles, so
+  // that waiting for them never waits for a tile): lane l holds hashes l and
+  // l + 64
   constexpr int SP = 32 * NCH;                 // slots per sorted array
   int va0 = INT_MAX, va1 = INT_MAX;            // a_i sorted (lane k: k-th, k+64-th)
   int ve0 = INT_MIN, ve1 = INT_MIN;            // e2_i sorted descending
   u32x4 aeL[PL ? NCH : 1][2];                  // e_i of slots 32 ch + 8 g .. + 7 (a order)
   u32x4 eaL[(PL && !CAUSAL) ? NCH : 1][2];     // a2_i of those slots (e2 order)
-  u32x4 pb[2];                                 // plan bits of hashes lane, lane + 64
-  int pa[2], pe[2];                            // their a (block of the first row) and e2
+  u32x4 pb[2];                                 // boundary bits
+  u32x4 pr[2];                                 // a, e, a2, e2
   int lo = 0, hi = n, cntA = 0;
   if constexpr (PL) {
     const size_t tix = static_cast<size_t>(h) * A.ntile + qt;
-    const int* mt = A.meta + tix * A.mstride;
     const PlanRec* rec = A.plan + tix * s;
-    lo = __builtin_amdgcn_readfirstlane(mt[META_LO]);
-    hi = __builtin_amdgcn_readfirstlane(mt[META_HI]);
-    cntA = __builtin_amdgcn_readfirstlane(mt[META_CNTA]);
-    const int* aa = mt + META_HDR;
-    va0 = aa[lane];
-    if constexpr (NCH == 4) va1 = aa[64 + lane];
-#pragma unroll
-    for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-      for (int x = 0; x < 2; ++x) aeL[ch][x] = *reinterpret_cast<const u32x4*>(aa + SP + 32 * ch + 8 * g + 4 * x);
-    if constexpr (!CAUSAL) {
-      ve0 = aa[2 * SP + lane];
-      if constexpr (NCH == 4) ve1 = aa[2 * SP + 64 + lane];
-#pragma unroll
-      for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-          eaL[ch][x] = *reinterpret_cast<const u32x4*>(aa + 3 * SP + 32 * ch + 8 * g + 4 * x);
-    }
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const int i = lane + 64 * x;
       const bool ok = (x == 0 || NCH == 4) && i < s;
       const PlanRec* ri = rec + (i < s ? i : 0);
       pb[x] = ok ? *reinterpret_cast<const u32x4*>(ri->bits) : u32x4{0, 0, 0, 0};
-      const u32x4 ae = *reinterpret_cast<const u32x4*>(ri);
-      pa[x] = ok ? static_cast<int>(ae[0]) : INT_MAX;
-      pe[x] = ok ? static_cast<int>(ae[3]) : INT_MIN;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ri);
+      // absent hashes: a = +inf, e = -inf, a2 = +inf, e2 = -inf (never count)
+      pr[x] = ok ? v : u32x4{0x7FFFFFFFu, 0x80000000u, 0x7FFFFFFFu, 0x80000000u};
     }
   }
 
@@ -623,8 +604,8 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
           const uint32_t b1 = __builtin_amdgcn_readlane(pb[x][1], i & 63);
           const uint32_t b2 = __builtin_amdgcn_readlane(pb[x][2], i & 63);
           const uint32_t b3 = __builtin_amdgcn_readlane(pb[x][3], i & 63);
-          const int ai = __builtin_amdgcn_readlane(pa[x], i & 63);
-          const int ei = __builtin_amdgcn_readlane(pe[x], i & 63);
+          const int ai = __builtin_amdgcn_readlane(static_cast<int>(pr[x][0]), i & 63);
+          const int ei = __builtin_amdgcn_readlane(static_cast<int>(pr[x][3]), i & 63);
           const uint64_t lo64 = b0 | (static_cast<uint64_t>(b1) << 32);
           const uint64_t hi64 = b2 | (static_cast<uint64_t>(b3) << 32);
           if ((lo64 | hi64) == 0) {  // one block over the whole tile
@@ -666,6 +647,60 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
       __hip_atomic_fetch_min(sLo + 64 + lane, lo1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       __hip_atomic_fetch_max(sHi + 64 + lane, hi1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
+    // the hashes in two orders for the far tiles (waves with the fewest
+    // hashes above): by the start a of the first row's block ascending, and
+    // (not causal) by the end e2 of the last row's block descending; ties by
+    // hash index.  Slots s .. SP-1 get sentinels that never count.
+    if (w == NW - 4 || (!CAUSAL && w == NW - 3)) {
+      const bool by_a = w == NW - 4;
+      int* sk = reinterpret_cast<int*>(sm + SM_SORT) + (by_a ? 0 : 2 * 128);
+      int* sv = sk + 128;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        if (x == 1 && NCH != 4) break;
+        const int i = lane + 64 * x;
+        // (-e2 is safe: e2 >= 1 for the hashes that take part)
+        const int key = by_a ? static_cast<int>(pr[x][0]) : (i < s ? -static_cast<int>(pr[x][3]) : 0);
+        int rank = 0;
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          if (y == 1 && NCH != 4) break;
+          const int kend = min(s, 64 * y + 64);
+          const int kv = by_a ? static_cast<int>(pr[y][0]) : (lane + 64 * y < s ? -static_cast<int>(pr[y][3]) : 0);
+          for (int k = 64 * y; k < kend; ++k) {
+            const int kk = __builtin_amdgcn_readlane(kv, k & 63);
+            rank += (kk < key) || (kk == key && k < i);
+          }
+        }
+        if (i < s) {
+          sk[rank] = by_a ? static_cast<int>(pr[x][0]) : static_cast<int>(pr[x][3]);
+          sv[rank] = by_a ? static_cast<int>(pr[x][1]) : static_cast<int>(pr[x][2]);
+        } else if (i < SP) {
+          sk[i] = by_a ? INT_MAX : INT_MIN;
+          sv[i] = by_a ? INT_MIN : INT_MAX;
+        }
+      }
+    }
+    // window of keys with weight, and the hashes whose first-row block starts
+    // left of the tile (every wave, from its registers)
+    {
+      int vlo = static_cast<int>(pr[0][0]), vhi = static_cast<int>(pr[0][3]);
+      int vca = static_cast<int>(pr[0][0]) < r0;
+      if constexpr (NCH == 4) {
+        vlo = min(vlo, static_cast<int>(pr[1][0]));
+        vhi = max(vhi, static_cast<int>(pr[1][3]));
+        vca += static_cast<int>(pr[1][0]) < r0;
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        vlo = min(vlo, __shfl_xor(vlo, o, 64));
+        vhi = max(vhi, __shfl_xor(vhi, o, 64));
+        vca += __shfl_xor(vca, o, 64);
+      }
+      lo = __builtin_amdgcn_readfirstlane(vlo);
+      hi = __builtin_amdgcn_readfirstlane(vhi);
+      cntA = __builtin_amdgcn_readfirstlane(vca);
+    }
     lds_barrier();
     // H operand through transposing reads of the [position][row] matrix:
     // source lane a + 4t of a 16-lane group reads rows 4a..4a+3 at position p0 + t
@@ -703,6 +738,26 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
       f.lo_r[rb] = reinterpret_cast<const int*>(sm + SM_LO)[f.rr[rb]];
       f.hi_r[rb] = reinterpret_cast<const int*>(sm + SM_HI)[f.rr[rb]];
       if constexpr (CAUSAL) f.hi_r[rb] = min(f.hi_r[rb], f.R[rb] + 1);
+    }
+    {
+      const int* sAa = reinterpret_cast<const int*>(sm + SM_SORT);
+      const int* sAe = sAa + 128;
+      const int* sEe = sAa + 256;
+      const int* sEa = sAa + 384;
+      va0 = sAa[lane];
+      if constexpr (NCH == 4) va1 = sAa[64 + lane];
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) aeL[ch][x] = *reinterpret_cast<const u32x4*>(sAe + 32 * ch + 8 * g + 4 * x);
+      if constexpr (!CAUSAL) {
+        ve0 = sEe[lane];
+        if constexpr (NCH == 4) ve1 = sEe[64 + lane];
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+          for (int x = 0; x < 2; ++x) eaL[ch][x] = *reinterpret_cast<const u32x4*>(sEa + 32 * ch + 8 * g + 4 * x);
+      }
     }
     // far operands: slot k of the a order counts for row r iff r < e_k; slot
     // k of the e2 order iff r >= a2_k (sentinel slots never count)
@@ -931,8 +986,6 @@ hipError_t launch_plsh_fwd(const void* q, const void* k, const void* v, void* o,
   FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.plan = reinterpret_cast<const PlanRec*>(static_cast<const char*>(bins) + L.off_plan);
-  a.meta = reinterpret_cast<const int*>(static_cast<const char*>(bins) + L.off_meta);
-  a.mstride = meta_stride_ints(s);
   a.B = batch; a.Hq = hq; a.Hkv = hkv; a.n = n; a.s = s;
   a.ntile = (n + BM - 1) / BM;
   const int grid = grid_size(a.ntile, batch * hq, &a.cs);
@@ -947,8 +1000,6 @@ hipError_t launch_alibi_fwd(const void* q, const void* k, const void* v, void* o
   FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.plan = nullptr;
-  a.meta = nullptr;
-  a.mstride = 0;
   a.B = batch; a.Hq = hq; a.Hkv = hkv; a.n = n; a.s = 1;
   a.ntile = (n + BM - 1) / BM;
   const int grid = grid_size(a.ntile, batch * hq, &a.cs);

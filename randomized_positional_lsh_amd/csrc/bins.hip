@@ -1,4 +1,4 @@
-// Bin-boundary kernels: from the hashes (delta, u) to the blocks they cut the
+// Bin-boundary kernel: from the hashes (delta, u) to the blocks they cut the
 // positions into.
 //
 // Positional LSH (explainer of arXiv 2605.09472, Methodology 1): random
@@ -176,83 +176,6 @@ __global__ __launch_bounds__(kThreads) void bins_kernel(const double* __restrict
   }
 }
 
-// Tile summaries: one wave per (head, query tile) merges the s plan records
-// of that tile.  The attention kernel takes from here the window of keys that
-// can carry weight, the hashes sorted by the start a of the block holding the
-// tile's first row (with their ends e), and sorted by the end e2 of the block
-// holding the last row, descending (with their starts a2).  Ties keep hash
-// order, so the summary is a deterministic function of the plan records.
-__global__ __launch_bounds__(256) void meta_kernel(const PlanRec* __restrict__ plan, int tiles, int s, int n,
-                                                   int ntile, int sp, int mstride, int32_t* __restrict__ meta) {
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (wid >= tiles) return;
-  const int qt = wid % ntile;
-  const int r0 = qt * kPlanTile, rlast = min(r0 + kPlanTile - 1, n - 1);
-  const PlanRec* rec = plan + static_cast<size_t>(wid) * s;  // records [h][qt][0..s)
-  int32_t* m = meta + static_cast<size_t>(wid) * mstride;
-
-  int a[2], e[2], a2[2], e2[2];
-  int lo = INT_MAX, hi = INT_MIN, afull = INT_MAX, efull = INT_MIN, cnta = 0;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int i = lane + 64 * k;
-    a[k] = INT_MAX; e[k] = INT_MIN; a2[k] = INT_MAX; e2[k] = INT_MIN;
-    if (i < s) {
-      a[k] = rec[i].a; e[k] = rec[i].e; a2[k] = rec[i].a2; e2[k] = rec[i].e2;
-      lo = min(lo, a[k]);
-      hi = max(hi, e2[k]);
-      if (e[k] > rlast) afull = min(afull, a[k]);    // first row's block covers every row
-      if (a2[k] <= r0) efull = max(efull, e2[k]);    // last row's block covers every row
-      cnta += a[k] < r0;
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    lo = min(lo, __shfl_xor(lo, o, 64));
-    hi = max(hi, __shfl_xor(hi, o, 64));
-    afull = min(afull, __shfl_xor(afull, o, 64));
-    efull = max(efull, __shfl_xor(efull, o, 64));
-    cnta += __shfl_xor(cnta, o, 64);
-  }
-  // ranks: by a ascending, by e2 descending, ties by hash index
-  int ra[2] = {0, 0}, re[2] = {0, 0};
-  for (int x = 0; x < s; ++x) {
-    const int ax = __shfl(x < 64 ? a[0] : a[1], x & 63, 64);
-    const int ex = __shfl(x < 64 ? e2[0] : e2[1], x & 63, 64);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int i = lane + 64 * k;
-      ra[k] += (ax < a[k]) || (ax == a[k] && x < i);
-      re[k] += (ex > e2[k]) || (ex == e2[k] && x < i);
-    }
-  }
-  int32_t* aa = m + META_HDR;
-  int32_t* ae = aa + sp;
-  int32_t* ee = ae + sp;
-  int32_t* ea = ee + sp;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int i = lane + 64 * k;
-    if (i < s) {
-      aa[ra[k]] = a[k];
-      ae[ra[k]] = e[k];
-      ee[re[k]] = e2[k];
-      ea[re[k]] = a2[k];
-    } else if (i < sp) {  // sentinels: never below a key, never above a row
-      aa[i] = INT_MAX;
-      ae[i] = INT_MIN;
-      ee[i] = INT_MIN;
-      ea[i] = INT_MAX;
-    }
-  }
-  if (lane < META_HDR) {
-    const int v = lane == META_LO ? lo : lane == META_HI ? hi : lane == META_AFULL ? afull
-                : lane == META_EFULL ? efull : lane == META_CNTA ? cnta : 0;
-    m[lane] = v;
-  }
-}
-
 }  // namespace
 
 BinsLayout bins_layout(int heads, int s, int n) {
@@ -263,8 +186,7 @@ BinsLayout bins_layout(int heads, int s, int n) {
   L.off_nblk = 0;
   L.off_starts = up(hs * sizeof(int32_t));
   L.off_plan = L.off_starts + up(hs * (static_cast<size_t>(n) + 1) * sizeof(int32_t));
-  L.off_meta = L.off_plan + up(static_cast<size_t>(heads) * ntile * s * sizeof(PlanRec));
-  L.total = L.off_meta + up(static_cast<size_t>(heads) * ntile * meta_stride_ints(s) * sizeof(int32_t));
+  L.total = L.off_plan + up(static_cast<size_t>(heads) * ntile * s * sizeof(PlanRec));
   return L;
 }
 
@@ -286,12 +208,6 @@ hipError_t launch_bins(const double* du, int heads, int s, int n, void* bins, hi
                      reinterpret_cast<int32_t*>(base + L.off_nblk),
                      reinterpret_cast<int32_t*>(base + L.off_starts),
                      reinterpret_cast<PlanRec*>(base + L.off_plan));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int tiles = heads * ntile;
-  hipLaunchKernelGGL(meta_kernel, dim3((tiles + 3) / 4), dim3(256), 0, stream,
-                     reinterpret_cast<const PlanRec*>(base + L.off_plan), tiles, s, n, ntile, meta_slots(s),
-                     meta_stride_ints(s), reinterpret_cast<int32_t*>(base + L.off_meta));
   return hipGetLastError();
 }
 

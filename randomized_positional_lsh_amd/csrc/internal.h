@@ -17,15 +17,8 @@ static_assert(sizeof(PlanRec) == 32, "plan record is 32 bytes");
 
 constexpr int kPlanTile = 128;
 
-// Tile summary of one (head, query tile): the hashes' plan records merged
-// for the attention kernel (layout documented in plpsh.h).  Slot arrays hold
-// meta_slots(s) entries; the unused ones carry sentinels.
-inline int meta_slots(int s) { return s <= 32 ? 32 : (s <= 64 ? 64 : 128); }
-inline int meta_stride_ints(int s) { return (8 + 4 * meta_slots(s) + 15) & ~15; }
-enum { META_LO = 0, META_HI = 1, META_AFULL = 2, META_EFULL = 3, META_CNTA = 4, META_HDR = 8 };
-
 struct BinsLayout {
-  size_t off_nblk, off_starts, off_plan, off_meta, total;
+  size_t off_nblk, off_starts, off_plan, total;
 };
 BinsLayout bins_layout(int heads, int s, int n);
 

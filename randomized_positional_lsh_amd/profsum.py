@@ -21,8 +21,7 @@ import json
 import os
 import statistics
 
-KERNELS = {"fwd_kernel": "attention (fwd_kernel)", "bins_kernel": "bin boundaries (bins_kernel)",
-           "meta_kernel": "tile summaries (meta_kernel)"}
+KERNELS = {"fwd_kernel": "attention (fwd_kernel)", "bins_kernel": "bin boundaries (bins_kernel)"}
 
 
 def _one(pattern: str) -> str:
