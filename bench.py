@@ -16,6 +16,11 @@ Prints ONE JSON line.  Besides the contract fields it carries:
   cpu_baseline : the fp64 oracle timed on a bounded sample of the same
                  workload on the host cores
   dense_alibi  : exact ALiBi (plpsh_alibi_dense_fwd) at the same n
+  literal      : the same step with the attention computed as one short
+                 attention per hash (plpsh_attention_fwd_literal, the
+                 reduction of Theorem 2.2 taken literally), same bins
+  fixed_blocks : the deterministic fixed-blocks baseline (plpsh_fixed_blocks_fwd,
+                 block b_h = round(2 sigma_h), the mean of Gamma(2, sigma_h))
   crossover    : PLSH vs dense ALiBi step times over n (Mistral shape)
 """
 
@@ -111,6 +116,14 @@ class Runner:
         if st:
             raise RuntimeError(self.P.status_string(st))
 
+    def attn_literal(self):
+        W = self.W
+        st = self.lib.plpsh_attention_fwd_literal(*self.vp, W.batch, W.heads_q, W.heads_kv, W.n, W.head_dim,
+                                                  self.dtype, W.s, int(W.causal), self.p_ws, self.nws, self.p_delta,
+                                                  self.stream)
+        if st:
+            raise RuntimeError(self.P.status_string(st))
+
     def attn(self):
         W = self.W
         st = self.lib.plpsh_attention_fwd_bins(*self.vp, W.batch, W.heads_q, W.heads_kv, W.n, W.head_dim, self.dtype,
@@ -194,6 +207,40 @@ def dense_alibi(P, W, q, k, v, steps=10, warmup=3):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / steps
+
+
+def literal(run, steps=10, warmup=3):
+    """Mean duration (ms) of the per-hash attention kernel on the bins of
+    the last timed step."""
+    import torch
+    for _ in range(warmup):
+        run.attn_literal()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        run.attn_literal()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def fixed_blocks(P, W, q, k, v, steps=10, warmup=3):
+    import numpy as np
+    import torch
+    block = np.maximum(1, np.rint(2.0 * np.asarray(W.sigmas, dtype=np.float64))).astype(np.int32)
+    o = torch.empty_like(q)
+    ws = torch.empty(P.workspace_bytes(W.heads_q, 1, W.n), dtype=torch.uint8, device=q.device)
+    for _ in range(warmup):
+        P.fixed_blocks(q, k, v, block, causal=W.causal, out=o, workspace=ws)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        P.fixed_blocks(q, k, v, block, causal=W.causal, out=o, workspace=ws)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps, block
 
 
 def crossover(P, synth, dev, ns, steps=5):
@@ -301,11 +348,20 @@ def main():
                    "sigma": "2^(8(h+1)/H)", "parallelism": "single GPU"},
         "roofline": roofline,
     }
+    lms = literal(run)
+    line["literal"] = {"kernel_ms": round(lms, 4), "fused_kernel_ms": round(kern_ms, 4),
+                       "slowdown_vs_fused": round(lms / kern_ms, 2)}
+    log(f"literal per-hash attention kernel {lms:.4f} ms")
     if not args.no_dense:
         dms = dense_alibi(P, W, q, k, v)
         line["dense_alibi"] = {"ms": round(dms, 4), "tokens_per_s": round(tokens / (dms * 1e-3), 1),
                                "speedup_plsh_vs_dense": round(dms / ms_step, 2)}
         log(f"dense exact ALiBi {dms:.4f} ms")
+        fms, block = fixed_blocks(P, W, q, k, v)
+        line["fixed_blocks"] = {"ms": round(fms, 4), "tokens_per_s": round(tokens / (fms * 1e-3), 1),
+                                "block": "round(2 sigma_h)", "block_min": int(block.min()),
+                                "block_max": int(block.max())}
+        log(f"fixed blocks {fms:.4f} ms")
     if not args.no_crossover and W.name == "mistral":
         del o
         line["crossover"] = crossover(P, synth, dev, [512, 1024, 2048, 4096, 8192, 16384, 32768, 65536])

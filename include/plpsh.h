@@ -208,6 +208,25 @@ plpsh_status plpsh_attention_fwd_hashes(const void* q, const void* k, const void
                                         void* stream);
 
 /*
+ * plpsh_fixed_blocks_fwd -- the "fixed blocks" baseline of the Mistral
+ * fine-tuning comparison (Key results, experimental validation): one
+ * deterministic partition of the positions into blocks of block[h] tokens
+ * per query head, attention inside each block only.  The same path as
+ * plpsh_attention_fwd_hashes with s = 1, delta = block[h], u = 0 (blocks
+ * [k b, (k + 1) b)).
+ *
+ *   block    : host [heads_q], each 1..PLPSH_MAX_N.
+ *   workspace: device, >= plpsh_workspace_bytes(heads_q, 1, n) bytes,
+ *              256-byte aligned; overwritten.
+ * Other arguments and errors as plpsh_attention_fwd.
+ */
+plpsh_status plpsh_fixed_blocks_fwd(const void* q, const void* k, const void* v, void* o,
+                                    int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                    int32_t n, int32_t head_dim, plpsh_dtype dtype,
+                                    const int32_t* block, int32_t causal,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * plpsh_attention_fwd_bins -- the attention step alone, on a bin buffer
  * already computed by plpsh_sample_bins / plpsh_bins_from_hashes for the
  * same (heads_q, s, n).  plpsh_attention_fwd is exactly plpsh_sample_bins
@@ -225,6 +244,24 @@ plpsh_status plpsh_attention_fwd_bins(const void* q, const void* k, const void* 
                                       int32_t n, int32_t head_dim, plpsh_dtype dtype,
                                       int32_t s, int32_t causal, const void* bins,
                                       size_t bins_bytes, const double* delta, void* stream);
+
+/*
+ * plpsh_attention_fwd_literal -- the same T~ computed as the reduction of
+ * Theorem 2.2 states it: one short, unbiased attention per hash, in which
+ * row r attends only to the keys of its own block of that hash, the s
+ * results summed with the shared causal mask C:
+ *   O_r = sum_i sum_{j in block_i(r)} C[r,j] e^{S[r,j]} v_j
+ *         / sum_i sum_{j in block_i(r)} C[r,j] e^{S[r,j]}
+ * which equals plpsh_attention_fwd_bins up to rounding order, at s times
+ * the logit work of the key tiles the blocks reach instead of one pass
+ * weighted by the counts.  An ablation of the fused kernel, not a faster
+ * path.  Arguments, layouts and errors exactly as plpsh_attention_fwd_bins.
+ */
+plpsh_status plpsh_attention_fwd_literal(const void* q, const void* k, const void* v, void* o,
+                                         int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                         int32_t n, int32_t head_dim, plpsh_dtype dtype,
+                                         int32_t s, int32_t causal, const void* bins,
+                                         size_t bins_bytes, const double* delta, void* stream);
 
 /*
  * plpsh_alibi_dense_fwd -- exact ALiBi attention T* (the quantity the

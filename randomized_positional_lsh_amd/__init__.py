@@ -12,10 +12,12 @@ from ._binding import (  # noqa: F401
     alibi_dense,
     attention,
     attention_from_bins,
+    attention_literal,
     attention_hashes,
     bins_from_hashes,
     bins_layout,
     draw_hashes,
+    fixed_blocks,
     raw,
     sample_bins,
     status_string,

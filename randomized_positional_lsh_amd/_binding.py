@@ -56,6 +56,10 @@ _SIGS = {
                                             _dp, _dp, _c_int, _c_int, _vp, _c_sz, _vp]),
     "plpsh_attention_fwd_bins": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                           _c_int, _c_int, _vp, _c_sz, _dp, _vp]),
+    "plpsh_attention_fwd_literal": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                             _c_int, _c_int, _vp, _c_sz, _dp, _vp]),
+    "plpsh_fixed_blocks_fwd": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                        ctypes.POINTER(ctypes.c_int32), _c_int, _vp, _c_sz, _vp]),
     "plpsh_alibi_dense_fwd": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _dp, _c_int, _vp]),
 }
@@ -243,21 +247,49 @@ def attention_hashes(q, k, v, delta, u, causal: bool = False, out=None, workspac
     return out
 
 
-def attention_from_bins(q, k, v, bins: "Bins", causal: bool = False, delta=None, out=None, stream=None):
-    """The attention step on a computed bin buffer (plpsh_attention_fwd_bins)."""
+def fixed_blocks(q, k, v, block, causal: bool = False, out=None, workspace=None, stream=None):
+    """The fixed-blocks baseline: blocks of block[h] positions per query head
+    (plpsh_fixed_blocks_fwd)."""
+    import numpy as np
+    import torch
+    B, Hq, Hkv, n, d = _qkv_shapes(q, k, v)
+    bl = np.ascontiguousarray(np.broadcast_to(np.asarray(block, dtype=np.int32), (Hq,)))
+    out = torch.empty_like(q) if out is None else out
+    ws = _workspace(workspace, Hq, 1, n, q.device)
+    st = _lib.plpsh_fixed_blocks_fwd(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                     ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()), B, Hq, Hkv, n, d,
+                                     _torch_dtype_code(q), bl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                     int(bool(causal)), ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream))
+    _check(st, "plpsh_fixed_blocks_fwd")
+    return out
+
+
+def _on_bins(fn, name, q, k, v, bins, causal, delta, out, stream):
     import torch
     B, Hq, Hkv, n, d = _qkv_shapes(q, k, v)
     if bins.heads != Hq or bins.n != n:
         raise ValueError("bins were computed for other sizes")
     dl = None if delta is None else _f64(delta)
     out = torch.empty_like(q) if out is None else out
-    st = _lib.plpsh_attention_fwd_bins(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
-                                       ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()), B, Hq, Hkv, n,
-                                       d, _torch_dtype_code(q), bins.s, int(bool(causal)),
-                                       ctypes.c_void_p(bins.buffer.data_ptr()), bins.buffer.numel(),
-                                       None if dl is None else _ptr(dl), _stream(stream))
-    _check(st, "plpsh_attention_fwd_bins")
+    st = fn(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+            ctypes.c_void_p(out.data_ptr()), B, Hq, Hkv, n, d, _torch_dtype_code(q), bins.s, int(bool(causal)),
+            ctypes.c_void_p(bins.buffer.data_ptr()), bins.buffer.numel(), None if dl is None else _ptr(dl),
+            _stream(stream))
+    _check(st, name)
     return out
+
+
+def attention_from_bins(q, k, v, bins: "Bins", causal: bool = False, delta=None, out=None, stream=None):
+    """The attention step on a computed bin buffer (plpsh_attention_fwd_bins)."""
+    return _on_bins(_lib.plpsh_attention_fwd_bins, "plpsh_attention_fwd_bins", q, k, v, bins, causal, delta, out,
+                    stream)
+
+
+def attention_literal(q, k, v, bins: "Bins", causal: bool = False, delta=None, out=None, stream=None):
+    """The same result as one short attention per hash over its blocks
+    (plpsh_attention_fwd_literal)."""
+    return _on_bins(_lib.plpsh_attention_fwd_literal, "plpsh_attention_fwd_literal", q, k, v, bins, causal, delta,
+                    out, stream)
 
 
 def alibi_dense(q, k, v, sigma, causal: bool = False, out=None, stream=None):

@@ -133,7 +133,7 @@ plpsh_status check_qkv(const void* q, const void* k, const void* v, void* o, int
 // widest bins (largest key windows) are scheduled first when delta is known.
 plpsh_status attention_on_bins(const void* q, const void* k, const void* v, void* o, int batch, int hq, int hkv,
                                int n, int d, int dtype, const double* delta, int s, int causal, const void* bins,
-                               hipStream_t st) {
+                               hipStream_t st, bool literal = false) {
   std::vector<uint16_t> order(hq);
   std::iota(order.begin(), order.end(), 0);
   if (delta) {
@@ -142,7 +142,8 @@ plpsh_status attention_on_bins(const void* q, const void* k, const void* v, void
       for (int i = 0; i < s; ++i) cost[h] += std::min(delta[h * s + i], static_cast<double>(n));
     std::stable_sort(order.begin(), order.end(), [&](uint16_t a, uint16_t b) { return cost[a] > cost[b]; });
   }
-  if (hip_failed(plpsh::launch_plsh_fwd(q, k, v, o, batch, hq, hkv, n, d, dtype, s, causal, bins, order.data(), st),
+  if (hip_failed(plpsh::launch_plsh_fwd(q, k, v, o, batch, hq, hkv, n, d, dtype, s, causal, bins, order.data(),
+                                        literal, st),
                  "attention kernel launch"))
     return PLPSH_ERR_HIP;
   return PLPSH_OK;
@@ -263,10 +264,24 @@ plpsh_status plpsh_attention_fwd_hashes(const void* q, const void* k, const void
                           workspace, stream);
 }
 
-plpsh_status plpsh_attention_fwd_bins(const void* q, const void* k, const void* v, void* o, int32_t batch,
-                                      int32_t heads_q, int32_t heads_kv, int32_t n, int32_t head_dim,
-                                      plpsh_dtype dtype, int32_t s, int32_t causal, const void* bins,
-                                      size_t bins_bytes, const double* delta, void* stream) {
+plpsh_status plpsh_fixed_blocks_fwd(const void* q, const void* k, const void* v, void* o, int32_t batch,
+                                    int32_t heads_q, int32_t heads_kv, int32_t n, int32_t head_dim,
+                                    plpsh_dtype dtype, const int32_t* block, int32_t causal, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (!block || heads_q < 1 || heads_q > 1024) return PLPSH_ERR_INVALID_ARGUMENT;
+  std::vector<double> delta(heads_q), u(heads_q, 0.0);
+  for (int h = 0; h < heads_q; ++h) {
+    if (block[h] < 1 || block[h] > PLPSH_MAX_N) return PLPSH_ERR_INVALID_ARGUMENT;
+    delta[h] = static_cast<double>(block[h]);
+  }
+  return plpsh_attention_fwd_hashes(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, delta.data(), u.data(),
+                                    1, causal, workspace, workspace_bytes, stream);
+}
+
+namespace {
+plpsh_status fwd_bins(const void* q, const void* k, const void* v, void* o, int32_t batch, int32_t heads_q,
+                      int32_t heads_kv, int32_t n, int32_t head_dim, plpsh_dtype dtype, int32_t s, int32_t causal,
+                      const void* bins, size_t bins_bytes, const double* delta, void* stream, bool literal) {
   plpsh_status r = check_qkv(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, causal);
   if (r != PLPSH_OK) return r;
   if (!valid_hs(heads_q, s)) return PLPSH_ERR_INVALID_ARGUMENT;
@@ -278,7 +293,24 @@ plpsh_status plpsh_attention_fwd_bins(const void* q, const void* k, const void* 
       if (!finite_pos(delta[i])) return PLPSH_ERR_INVALID_ARGUMENT;
   }
   return attention_on_bins(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, delta, s, causal, bins,
-                           static_cast<hipStream_t>(stream));
+                           static_cast<hipStream_t>(stream), literal);
+}
+}  // namespace
+
+plpsh_status plpsh_attention_fwd_bins(const void* q, const void* k, const void* v, void* o, int32_t batch,
+                                      int32_t heads_q, int32_t heads_kv, int32_t n, int32_t head_dim,
+                                      plpsh_dtype dtype, int32_t s, int32_t causal, const void* bins,
+                                      size_t bins_bytes, const double* delta, void* stream) {
+  return fwd_bins(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, s, causal, bins, bins_bytes, delta,
+                  stream, false);
+}
+
+plpsh_status plpsh_attention_fwd_literal(const void* q, const void* k, const void* v, void* o, int32_t batch,
+                                         int32_t heads_q, int32_t heads_kv, int32_t n, int32_t head_dim,
+                                         plpsh_dtype dtype, int32_t s, int32_t causal, const void* bins,
+                                         size_t bins_bytes, const double* delta, void* stream) {
+  return fwd_bins(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, s, causal, bins, bins_bytes, delta,
+                  stream, true);
 }
 
 plpsh_status plpsh_alibi_dense_fwd(const void* q, const void* k, const void* v, void* o, int32_t batch,

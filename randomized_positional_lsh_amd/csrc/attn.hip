@@ -73,7 +73,7 @@ constexpr int NT = 64 * NW;   // threads per workgroup
 constexpr int BN = 64;     // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 
-enum { MODE_PLSH = 0, MODE_ALIBI = 1 };
+enum { MODE_PLSH = 0, MODE_ALIBI = 1, MODE_LITERAL = 2 };
 enum { KIND_NEAR = 0, KIND_LEFT = 1, KIND_RIGHT = 2 };
 
 // heads, most expensive first, two 16-bit entries per word (dword elements
@@ -471,6 +471,7 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
   using T = typename G::T;
   using F = Fwd<D, BF, CAUSAL, NCH, MODE>;
   constexpr bool PL = MODE == MODE_PLSH;
+  constexpr bool LIT = MODE == MODE_LITERAL;
   constexpr int KS = G::KS, DB = G::DB;
 
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
@@ -516,7 +517,7 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
   u32x4 pb[2];                                 // boundary bits
   u32x4 pr[2];                                 // a, e, a2, e2
   int lo = 0, hi = n, cntA = 0;
-  if constexpr (PL) {
+  if constexpr (PL || LIT) {
     const size_t tix = static_cast<size_t>(h) * A.ntile + qt;
     const PlanRec* rec = A.plan + tix * s;
 #pragma unroll
@@ -535,7 +536,7 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
   // right after the first barrier of the count set-up, which would wait for it
   TileLoader<D, BF> ld;
   ld.init(w, lane);
-  if constexpr (!PL) ld.issue(Kh, Vh, r0, n, stage0, w);
+  if constexpr (MODE == MODE_ALIBI) ld.issue(Kh, Vh, r0, n, stage0, w);
 
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
@@ -783,7 +784,7 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
     }
   }
 
-  if constexpr (!PL) {
+  if constexpr (MODE == MODE_ALIBI) {
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       f.lo_r[rb] = 0;
@@ -807,7 +808,7 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
 
   // ---- softmax state
   f.sc = rsqrtf(static_cast<float>(D)) * kLog2e;  // logit -> log2 units
-  f.scp = PL ? f.sc : 1.0f;                        // scale applied at exp time
+  f.scp = MODE == MODE_ALIBI ? 1.0f : f.sc;        // scale applied at exp time
   f.thr = 8.0f / f.scp;                            // rescale margin (units of x)
   f.beta = MODE == MODE_ALIBI ? hsc.beta[h] : 0.0f;
 #pragma unroll
@@ -828,6 +829,75 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
     __syncthreads();
     if (t + 1 < ntl) ld.issue(Kh, Vh, tile_j0(t + 1), n, (t & 1) ? stage0 : stage1, w);
   };
+  if constexpr (LIT) {
+    // One short attention per hash, as in the reduction of Theorem 2.2: for
+    // hash i, row r attends to the keys of its own block of hash i.  The
+    // partial sums of all hashes share one running maximum, so they add up
+    // to the count-weighted sums with no merge step; the logits of a key
+    // tile are recomputed for every hash whose blocks reach it.
+    auto recv = [&](int i, int c) {
+      return __builtin_amdgcn_readlane(static_cast<int>(i < 64 ? pr[0][c] : pr[1][c]), i & 63);
+    };
+    // keys of hash i that some row of the tile attends to: [a_i, e2_i)
+    auto span = [&](int i, int& ja, int& je) {
+      ja = recv(i, 0);
+      je = recv(i, 3);
+      if constexpr (CAUSAL) je = min(je, r0 + nrows);
+    };
+    // each row's block of hash i: the last boundary at or before the row
+    // (else a_i) and the first boundary after it (else e2_i)
+    auto set_hash = [&](int i) {
+      const uint32_t b0 = __builtin_amdgcn_readlane(i < 64 ? pb[0][0] : pb[1][0], i & 63);
+      const uint32_t b1 = __builtin_amdgcn_readlane(i < 64 ? pb[0][1] : pb[1][1], i & 63);
+      const uint32_t b2 = __builtin_amdgcn_readlane(i < 64 ? pb[0][2] : pb[1][2], i & 63);
+      const uint32_t b3 = __builtin_amdgcn_readlane(i < 64 ? pb[0][3] : pb[1][3], i & 63);
+      const int ai = recv(i, 0), ei = recv(i, 3);
+      const uint64_t lo64 = b0 | (static_cast<uint64_t>(b1) << 32);
+      const uint64_t hi64 = b2 | (static_cast<uint64_t>(b3) << 32);
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const int p = f.rr[rb];
+        const int q = p & 63;
+        const uint64_t le = q == 63 ? ~0ull : ((2ull << q) - 1);
+        const uint64_t half = p < 64 ? lo64 : hi64;
+        const uint64_t m = half & le, gt = half & ~le;
+        int st = m ? (p & 64) + 63 - __builtin_clzll(m) : ((p >= 64 && lo64) ? 63 - __builtin_clzll(lo64) : 0);
+        int en = gt ? (p & 64) + __builtin_ctzll(gt) : ((p < 64 && hi64) ? 64 + __builtin_ctzll(hi64) : BM);
+        f.lo_r[rb] = st ? r0 + st : ai;
+        f.hi_r[rb] = en < BM ? r0 + en : ei;
+        if constexpr (CAUSAL) f.hi_r[rb] = min(f.hi_r[rb], f.R[rb] + 1);
+      }
+      f.loF = __builtin_amdgcn_readlane(f.lo_r[0], 0);
+      f.hiF = __builtin_amdgcn_readlane(f.hi_r[0], 0);
+      f.loL = __builtin_amdgcn_readlane(f.lo_r[NRB - 1], 15);
+      f.hiL = __builtin_amdgcn_readlane(f.hi_r[NRB - 1], 15);
+    };
+    const int mkey0[4] = {0, 0, 0, 0};
+    int i = 0, j0, jend;
+    span(0, j0, jend);
+    ld.issue(Kh, Vh, j0, n, stage0, w);
+    set_hash(0);
+    for (int t = 0;; ++t) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      // the next (hash, tile) goes to the other stage, which every wave is done with
+      int ni = i, nj = j0 + BN, nje = jend;
+      if (nj >= jend) {
+        ni = i + 1;
+        if (ni < s) span(ni, nj, nje);
+      }
+      if (ni < s) ld.issue(Kh, Vh, nj, n, (t & 1) ? stage0 : stage1, w);
+      const unsigned char* st = (t & 1) ? stage1 : stage0;
+      f.begin_k(st);
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) f.template chunk<KIND_NEAR, 0>(st, st + G::TILE, j0, r0, n, kc, mkey0, hf);
+      if (ni >= s) break;
+      if (ni != i) set_hash(ni);
+      i = ni;
+      j0 = nj;
+      jend = nje;
+    }
+  } else {
   int t = 0;
   {
     // the near tiles: keys r0 .. r0 + 63 in stage 0, r0 + 64 .. r0 + 127 in stage 1
@@ -908,6 +978,7 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
       for (int kc = 0; kc < 2; ++kc) f.template chunk<KIND_RIGHT, 0>(st, st + G::TILE, j0, r0, n, kc, mkey, cb);
     }
   }
+  }
 
   // ---- epilogue: O_r = acc / l
 #pragma unroll
@@ -947,6 +1018,8 @@ template <int D, bool BF, bool CAUSAL, int MODE>
 hipError_t dispatch_nch(const FwdArgs& a, const HeadOrder& o, const HeadScale& hs, int grid, hipStream_t st) {
   if constexpr (MODE == MODE_ALIBI) {
     return launch_one<D, BF, CAUSAL, 1, MODE>(a, o, hs, grid, st);
+  } else if constexpr (MODE == MODE_LITERAL) {
+    return launch_one<D, BF, CAUSAL, 4, MODE>(a, o, hs, grid, st);  // both plan-record registers loaded
   } else {
     if (a.s <= 32) return launch_one<D, BF, CAUSAL, 1, MODE>(a, o, hs, grid, st);
     if (a.s <= 64) return launch_one<D, BF, CAUSAL, 2, MODE>(a, o, hs, grid, st);
@@ -981,7 +1054,7 @@ int grid_size(int ntile, int instances, int* cs) {
 
 hipError_t launch_plsh_fwd(const void* q, const void* k, const void* v, void* o, int batch, int hq, int hkv,
                            int n, int d, int dtype, int s, int causal, const void* bins, const uint16_t* order,
-                           hipStream_t st) {
+                           bool literal, hipStream_t st) {
   const BinsLayout L = bins_layout(hq, s, n);
   FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o;
@@ -992,6 +1065,7 @@ hipError_t launch_plsh_fwd(const void* q, const void* k, const void* v, void* o,
   HeadOrder ord{};
   for (int i = 0; i < hq; ++i) ord.set(i, order[i]);
   HeadScale hs{};
+  if (literal) return dispatch<MODE_LITERAL>(a, ord, hs, d, dtype, causal, grid, st);
   return dispatch<MODE_PLSH>(a, ord, hs, d, dtype, causal, grid, st);
 }
 

@@ -32,7 +32,7 @@ hipError_t launch_bins(const double* du, int heads, int s, int n, void* bins, hi
 hipError_t launch_plsh_fwd(const void* q, const void* k, const void* v, void* o,
                            int batch, int hq, int hkv, int n, int d, int dtype,
                            int s, int causal, const void* bins, const uint16_t* head_order,
-                           hipStream_t st);
+                           bool literal, hipStream_t st);
 
 hipError_t launch_alibi_fwd(const void* q, const void* k, const void* v, void* o,
                             int batch, int hq, int hkv, int n, int d, int dtype,

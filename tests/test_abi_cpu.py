@@ -133,6 +133,22 @@ def test_hashes_validation():
     assert st == B.WORKSPACE_TOO_SMALL
 
 
+def test_fixed_blocks_validation():
+    lib = B.raw()
+    i32 = ctypes.POINTER(ctypes.c_int32)
+    for bad in ([16, 0], [16, -3], [16, B.MAX_N + 1]):
+        bl = np.array(bad, dtype=np.int32)
+        st = lib.plpsh_fixed_blocks_fwd(FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 64, 64, 1, bl.ctypes.data_as(i32), 0,
+                                        FAKE, 1 << 30, None)
+        assert st == B.INVALID_ARGUMENT, bad
+    assert lib.plpsh_fixed_blocks_fwd(FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 64, 64, 1, None, 0, FAKE, 1 << 30,
+                                      None) == B.INVALID_ARGUMENT
+    bl = np.array([16, 128], dtype=np.int32)
+    st = lib.plpsh_fixed_blocks_fwd(FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 64, 64, 1, bl.ctypes.data_as(i32), 0, FAKE, 10,
+                                    None)
+    assert st == B.WORKSPACE_TOO_SMALL
+
+
 def test_draw_validation():
     lib = B.raw()
     sig = np.array([1.0])

@@ -210,13 +210,59 @@ def test_single_position_blocks_return_v_exactly(gpu, dtype):
 def test_fixed_blocks(gpu):
     """s = 1, delta = b, u = 0: deterministic partition into blocks of b."""
     (q, k, v), (q64, k64, v64) = _qkv_dev(1, 2, 2, 500, 128, "bf16", 5, gpu)
-    delta = np.array([[16.0], [128.0]])
+    block = np.array([16, 128], dtype=np.int32)
+    delta = block.astype(np.float64)[:, None]
     u = np.zeros((2, 1))
     for causal in (False, True):
-        o = P.attention_hashes(q, k, v, delta, u, causal=causal)
+        o = P.fixed_blocks(q, k, v, block, causal=causal)
+        o2 = P.attention_hashes(q, k, v, delta, u, causal=causal)
         torch.cuda.synchronize()
         ref = oracle.plsh_attention(q64, k64, v64, delta, u, causal)
         check_slices(to64(o), ref, "bf16", where=f"fixed blocks causal={causal}")
+        assert torch.equal(o, o2), f"fixed blocks vs one deterministic hash, causal={causal}"
+
+
+LITERAL_CASES = [CASES[i] for i in (0, 3, 4, 5, 6, 8, 9, 10, 11, 12)]
+
+
+@pytest.mark.parametrize("case", LITERAL_CASES,
+                         ids=lambda c: f"B{c[0]}H{c[1]}/{c[2]}n{c[3]}d{c[4]}{c[5]}s{c[7]}{'c' if c[8] else 'nc'}")
+def test_literal_matches_literal_oracle(gpu, case):
+    """The per-hash short-attention kernel against the oracle's per-block
+    formulation (Theorem 2.2), every output element."""
+    B, Hq, Hkv, n, d, dtype, sig, s, causal = case
+    say(f"literal small case {case}")
+    (q, k, v), (q64, k64, v64) = _qkv_dev(B, Hq, Hkv, n, d, dtype, 7 + n, gpu, scale_q=2.0)
+    delta, u, bins = P.sample_bins(11, sig, s, n, device=gpu)
+    o = torch.full_like(q, float("nan"))
+    P.attention_literal(q, k, v, bins, causal=causal, delta=delta, out=o)
+    torch.cuda.synchronize()
+    ref = oracle.plsh_attention_literal(q64, k64, v64, delta, u, causal)
+    err = check_slices(to64(o), ref, dtype, where=f"literal {case}")
+    say(f"  max err {err:.3e}")
+
+
+def test_literal_full_size_sampled_rows(gpu):
+    W = synth.WORKLOADS["mistral"]
+    say("literal kernel, mistral full size, sampled rows")
+    q, k, v = synth.qkv_torch(W.batch, W.heads_q, W.heads_kv, W.n, W.head_dim, W.dtype, W.data_seed, gpu)
+    delta, u, bins = P.sample_bins(W.hash_seed, W.sigmas, W.s, W.n, device=gpu)
+    o = torch.full_like(q, float("nan"))
+    P.attention_literal(q, k, v, bins, causal=W.causal, delta=delta, out=o)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any().item(), "output not fully written"
+    rng = np.random.default_rng(9)
+    grp = W.heads_q // W.heads_kv
+    worst = 0.0
+    for h in range(0, W.heads_q, 2):
+        rows = sample_rows(W.n, 12, rng)
+        kh = to64(k[0, h // grp])
+        vh = to64(v[0, h // grp])
+        qh = to64(q[0, h, torch.as_tensor(rows, device=gpu)])
+        ref = oracle.plsh_attention_rows(qh, kh, vh, delta[h], u[h], rows, W.causal)
+        got = to64(o[0, h, torch.as_tensor(rows, device=gpu)])
+        worst = max(worst, check_slices(got[None], ref[None], W.dtype, where=f"literal mistral head {h}"))
+    say(f"  worst rel err {worst:.3e}")
 
 
 def test_deterministic_and_canary(gpu):
