@@ -32,6 +32,11 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is missing: build it with `python randomized_positional_lsh_amd/build.py` "
         "(hipcc, gfx950). There is no fallback implementation.")
 
+# torch is loaded first so that libplpsh binds to the HIP runtime torch has
+# already mapped (same soname) instead of mapping a second copy: a process
+# with two HIP runtimes can find no device in the one initialised second.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 _c_int = ctypes.c_int32

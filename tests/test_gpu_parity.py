@@ -277,6 +277,34 @@ def test_deterministic_and_canary(gpu):
     assert torch.equal(o1, o2)
 
 
+def test_repeated_launches_across_sizes_and_streams(gpu):
+    """Launches of different sizes and kinds in a row, and spread over two
+    streams, reproduce the results of launches made one at a time."""
+    W = synth.WORKLOADS["small"]
+    shapes = [(1, 8, 8, 1500, 64), (2, 4, 2, 200, 64), (1, 8, 8, 1500, 64), (1, 2, 1, 1, 64), (1, 4, 4, 9000, 64)]
+    data = [_qkv_dev(*sh, "bf16", 20 + i, gpu)[0] for i, sh in enumerate(shapes)]
+    sig = [np.asarray(W.sigmas[:sh[1]]) for sh in shapes]
+    ref = []
+    for (q, k, v), sg in zip(data, sig):
+        ref.append(P.attention(q, k, v, sg, 10, seed=3, causal=True))
+        torch.cuda.synchronize()
+    ref.append(P.alibi_dense(*data[1], sig[1], causal=False))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        outs = []
+        for i, ((q, k, v), sg) in enumerate(zip(data, sig)):
+            st = streams[(i + rep) % 2]
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                outs.append(P.attention(q, k, v, sg, 10, seed=3, causal=True, stream=st))
+        with torch.cuda.stream(streams[rep % 2]):
+            outs.append(P.alibi_dense(*data[1], sig[1], causal=False, stream=streams[rep % 2]))
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, ref)):
+            assert torch.equal(a, b), f"launch {i}, repetition {rep}"
+
+
 def test_empty_inputs(gpu):
     q = torch.zeros((0, 2, 16, 64), dtype=torch.bfloat16, device=gpu)
     o = P.attention(q, q[:, :1], q[:, :1], [2.0, 3.0], 4, causal=True)
