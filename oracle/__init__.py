@@ -22,6 +22,10 @@ and Japanese with the same section structure:
 * [P, Key results]     O(1/sqrt(s)) error decay; experiments
 * [P, Limitations]     no wall-clock claim against dense kernels
 
+``oracle.convergence`` gives the error E = L* - M~ of [P, Theorem 2.1] at
+sequence lengths where dense matrices no longer fit (row maxima, products
+E x, spectral norm).
+
 Parity status of each function is stated in its docstring; all functions
 here are pinned by ``tests/test_oracle_pins.py`` (closed forms, exact
 rational arithmetic, brute force, special cases reducing to library
@@ -44,3 +48,10 @@ from .plsh import (  # noqa: F401
     support_interval,
 )
 from .sampler import splitmix64, sample_hashes  # noqa: F401
+from .convergence import (  # noqa: F401
+    error_dense,
+    error_matvec,
+    error_maxnorm,
+    error_rowmax,
+    error_spectral,
+)

@@ -453,3 +453,59 @@ def test_rows_and_bands_equal_dense(causal):
     assert np.abs(band - dense).max() < 1e-12
     Ts = oracle.alibi_attention(q, k, v, [12.0], causal)[0, 0]
     assert np.abs(oracle.alibi_attention_rows(q[0, 0], k[0, 0], v[0, 0], 12.0, rows, causal) - Ts[rows]).max() < 1e-12
+
+
+# ---------------------------------------------------------------- P13 ------
+# [P, Theorem 2.1; Key results, experimental validation]: the error
+# E = L* - M~ at large n.  The large-n forms (row maxima from the
+# definition, E x through the Toeplitz product and per-bin sums, ARPACK
+# spectral norm) must agree with the dense matrices, and with closed forms.
+
+@pytest.mark.parametrize("n", [300, 777])
+def test_p13_error_matvec_equals_dense(n):
+    rng = _rng(21 + n)
+    sigma = 9.0
+    dl, uu = _draw(rng, sigma, 7)
+    dl = np.append(dl, [0.5, 3.0 * n])        # single-position blocks; one block
+    uu = np.append(uu, [0.25, 0.0])
+    x = rng.standard_normal(n)
+    E = oracle.error_dense(sigma, dl, uu, n)
+    y = oracle.error_matvec(sigma, dl, uu, n, x)
+    assert np.abs(y - E @ x).max() <= 1e-12 * np.abs(E @ x).max()
+
+
+def test_p13_error_rowmax_equals_dense():
+    rng = _rng(23)
+    n, sigma = 300, 12.0
+    dl, uu = _draw(rng, sigma, 9)
+    E = oracle.error_dense(sigma, dl, uu, n)
+    rows = np.arange(n)
+    assert np.array_equal(oracle.error_rowmax(sigma, dl, uu, n, rows), np.abs(E).max(axis=1))
+    assert oracle.error_maxnorm(sigma, dl, uu, n) == np.abs(E).max()
+
+
+def test_p13_error_spectral_arpack_equals_dense():
+    rng = _rng(24)
+    n, sigma = 500, 10.0
+    dl, uu = _draw(rng, sigma, 5)
+    dense = np.linalg.norm(oracle.error_dense(sigma, dl, uu, n), 2)
+    arpack = oracle.error_spectral(sigma, dl, uu, n, dense_below=0)
+    assert abs(arpack - dense) <= 1e-9 * dense
+
+
+def test_p13_closed_forms():
+    """One block over everything: E = L* - J, whose largest entry is at the
+    corners, 1 - exp(-(n-1)/sigma).  Single-position blocks: M~ = I, so the
+    largest entry is exp(-1/sigma) and ||E||_2 = ||L* - I||_2 lies below the
+    Toeplitz-symbol bound 2 rho / (1 - rho), rho = exp(-1/sigma), and tends
+    to it as n grows."""
+    n, sigma = 400, 25.0
+    assert math.isclose(oracle.error_maxnorm(sigma, [2.0 * n], [0.0], n), 1 - math.exp(-(n - 1) / sigma),
+                        rel_tol=1e-14)
+    assert math.isclose(oracle.error_maxnorm(sigma, [0.5, 0.9], [0.1, 0.3], n), math.exp(-1 / sigma),
+                        rel_tol=1e-14)
+    n, sigma = 4096, 4.0
+    rho = math.exp(-1 / sigma)
+    bound = 2 * rho / (1 - rho)
+    spec = oracle.error_spectral(sigma, [0.5], [0.0], n)      # ARPACK path (n >= 2048)
+    assert 0.999 * bound < spec < bound
