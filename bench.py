@@ -22,6 +22,9 @@ Prints ONE JSON line.  Besides the contract fields it carries:
   fixed_blocks : the deterministic fixed-blocks baseline (plpsh_fixed_blocks_fwd,
                  block b_h = round(2 sigma_h), the mean of Gamma(2, sigma_h))
   crossover    : PLSH vs dense ALiBi step times over n (Mistral shape)
+  convergence  : ||L* - M~||_2 and ||L* - M~||_max against s at n = 131072,
+                 sigma = 256 (plpsh_error_norms), with the fitted log-log
+                 slopes and the time per measurement
 """
 
 from __future__ import annotations
@@ -266,6 +269,40 @@ def crossover(P, synth, dev, ns, steps=5):
     return out
 
 
+def convergence(P, dev, n=131072, sigma=256.0, ss=(2, 4, 8, 16, 32, 64, 128), seeds=3, max_steps=400):
+    """Both error norms of the mask mean against L* over s, one head."""
+    import numpy as np
+    import torch
+    import synth
+    out = {"n": n, "sigma": sigma, "s": list(ss), "seeds": seeds, "spectral": [], "maxnorm": [], "ms": [],
+           "lanczos_steps": [], "lanczos_converged": []}
+    ws = torch.empty(P.error_workspace_bytes(n, max(ss), max_steps), dtype=torch.uint8, device=dev)
+    for s in ss:
+        sp, mx, ms, st = [], [], [], []
+        for seed in range(seeds):
+            delta, u = P.draw_hashes(1000 + seed, [sigma], s)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            r = P.error_norms(sigma, delta[0], u[0], n, max_steps=max_steps, tol=1e-9, seed=seed, workspace=ws)
+            ms.append(1e3 * (time.perf_counter() - t0))
+            sp.append(r["spectral"])
+            mx.append(r["maxnorm"])
+            st.append(r["steps"])
+        out["spectral"].append(float(np.mean(sp)))
+        out["maxnorm"].append(float(np.mean(mx)))
+        out["ms"].append(round(float(np.mean(ms)), 2))
+        out["lanczos_steps"].append(int(np.max(st)))
+        out["lanczos_converged"].append(bool(np.max(st) < max_steps))
+    # log-log slopes over s >= 8, past the small-s regime where the max norm sits near 1
+    sel = np.asarray(ss) >= 8
+    ls = np.log(np.asarray(ss, dtype=np.float64))[sel]
+    out["slope_spectral"] = round(float(np.polyfit(ls, np.log(np.asarray(out["spectral"])[sel]), 1)[0]), 3)
+    out["slope_maxnorm"] = round(float(np.polyfit(ls, np.log(np.asarray(out["maxnorm"])[sel]), 1)[0]), 3)
+    out["spectral"] = [round(x, 6) for x in out["spectral"]]
+    out["maxnorm"] = [round(x, 6) for x in out["maxnorm"]]
+    return out
+
+
 def copy_calibration(dev, nbytes=1 << 30, reps=5):
     """A plain device copy of known size, for scaling HBM counters."""
     import torch
@@ -287,6 +324,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-crossover", action="store_true")
+    ap.add_argument("--no-convergence", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true", help="only run a 1 GiB device copy (counter scaling)")
     args = ap.parse_args()
 
@@ -366,6 +404,9 @@ def main():
         del o
         line["crossover"] = crossover(P, synth, dev, [512, 1024, 2048, 4096, 8192, 16384, 32768, 65536])
         log(f"crossover {line['crossover']}")
+    if not args.no_convergence:
+        line["convergence"] = convergence(P, dev)
+        log(f"convergence {line['convergence']}")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(W, q, k, v, delta, u, args.cpu_seconds)
         log(f"cpu baseline {line['cpu_baseline']}")

@@ -276,6 +276,64 @@ plpsh_status plpsh_alibi_dense_fwd(const void* q, const void* k, const void* v, 
                                    int32_t n, int32_t head_dim, plpsh_dtype dtype,
                                    const double* sigma, int32_t causal, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Error of the mask mean against the bias matrix at large n.
+ *
+ * E = L* - M~ for one head, with L*[r, j] = exp(-|r - j| / sigma) (the
+ * exponentiated ALiBi bias, Methodology 1) and M~ = c / s the mean of the
+ * head's s sampled masks (Theorem 2.1).  The pages state that ||E||_2 and
+ * ||E||_max fall like 1/sqrt(s) and that their experiments saw the matrix
+ * error go to zero as s grows (Key results, experimental validation); these
+ * calls measure both norms without forming E (O(n s) memory and work per
+ * product).  All arithmetic is IEEE binary64.
+ *
+ *   sigma : finite, > 0.   n: 1..PLPSH_MAX_N.   s: 1..PLPSH_MAX_S.
+ *   bins  : device bin buffer of ONE head (heads = 1) for these (s, n),
+ *           written by plpsh_bins_from_hashes / plpsh_sample_bins,
+ *           256-byte aligned, >= plpsh_bins_bytes(1, s, n) bytes.
+ * ------------------------------------------------------------------------ */
+
+/* Workspace for plpsh_error_matvec (max_steps = 0) or plpsh_error_norms
+ * (max_steps >= 1, at most 1000); 0 for invalid sizes. */
+size_t plpsh_error_workspace_bytes(int32_t n, int32_t s, int32_t max_steps);
+
+/*
+ * plpsh_error_rowmax -- rowmax[r] = max_j |L*[r, j] - c[r, j] / s|, for
+ * r in [0, n).  rowmax: device, n doubles (caller-owned).  Asynchronous on
+ * `stream`.
+ */
+plpsh_status plpsh_error_rowmax(double sigma, int32_t n, int32_t s, const void* bins, size_t bins_bytes,
+                                double* rowmax, void* stream);
+
+/*
+ * plpsh_error_matvec -- y = E x for device vectors x, y of n doubles (no
+ * overlap).  workspace: device, 256-byte aligned, >=
+ * plpsh_error_workspace_bytes(n, s, 0) bytes.  Asynchronous on `stream`.
+ */
+plpsh_status plpsh_error_matvec(double sigma, int32_t n, int32_t s, const void* bins, size_t bins_bytes,
+                                const double* x, double* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * plpsh_error_norms -- both norms of E for the hashes (delta[i], u[i]),
+ * i < s (host arrays, as plpsh_bins_from_hashes).
+ *   maxnorm    : host out, ||E||_max (exact, from the row maxima);
+ *   argmax_row : host out or NULL, the first row where it is attained;
+ *   spectral   : host out, ||E||_2 = max |eigenvalue| of the symmetric E,
+ *                by Lanczos with full reorthogonalisation from a start
+ *                vector drawn from `seed`; it stops when the estimate has
+ *                changed by at most tol (relative) over three steps, the
+ *                Krylov space closes, or after max_steps (1..1000) steps;
+ *   steps      : host out or NULL, Lanczos steps taken.
+ * workspace: device, 256-byte aligned, >= plpsh_error_workspace_bytes(n, s,
+ * max_steps) bytes (holds the bins, max_steps + 1 Lanczos vectors and
+ * scratch).  Synchronises `stream` (the iteration reads scalars back every
+ * step).
+ */
+plpsh_status plpsh_error_norms(double sigma, int32_t n, int32_t s, const double* delta, const double* u,
+                               int32_t max_steps, double tol, uint64_t seed, void* workspace, size_t workspace_bytes,
+                               double* spectral, double* maxnorm, int32_t* argmax_row, int32_t* steps,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ import numpy as np
 
 from .plsh import alibi_matrix, bin_values, mtilde
 
-__all__ = ["error_dense", "error_rowmax", "error_matvec", "error_spectral", "error_maxnorm"]
+__all__ = ["ErrorOperator", "error_dense", "error_rowmax", "error_matvec", "error_spectral", "error_maxnorm"]
 
 
 def _hashes(deltas, us):
@@ -69,23 +69,34 @@ def _laplace_column(sigma: float, n: int) -> np.ndarray:
     return np.exp(-np.arange(n, dtype=np.float64) / float(sigma))
 
 
-def error_matvec(sigma: float, deltas, us, n: int, x) -> np.ndarray:
-    """E x = L* x - (1/s) sum_i M(h_i) x.
+class ErrorOperator:
+    """x -> E x = L* x - (1/s) sum_i M(h_i) x.
 
     L* is the symmetric Toeplitz matrix whose first column is exp(-k/sigma);
-    (M(h_i) x)[r] is the sum of x over the positions sharing r's bin.
+    (M(h_i) x)[r] is the sum of x over the positions sharing r's bin.  The
+    bin labels of each hash are computed once.
     """
-    from scipy.linalg import matmul_toeplitz
 
-    d, u = _hashes(deltas, us)
-    x = np.asarray(x, dtype=np.float64)
-    lx = matmul_toeplitz(_laplace_column(sigma, n), x)
-    mx = np.zeros(n)
-    for dl, uu in zip(d, u):
-        b = bin_values(dl, uu, n)
-        _, inv = np.unique(b, return_inverse=True)
-        mx += np.bincount(inv, weights=x)[inv]
-    return lx - mx / d.size
+    def __init__(self, sigma: float, deltas, us, n: int):
+        d, u = _hashes(deltas, us)
+        self.n, self.s = n, d.size
+        self.col = _laplace_column(sigma, n)
+        self.labels = [np.unique(bin_values(dl, uu, n), return_inverse=True)[1] for dl, uu in zip(d, u)]
+
+    def matvec(self, x) -> np.ndarray:
+        from scipy.linalg import matmul_toeplitz
+
+        x = np.asarray(x, dtype=np.float64).reshape(-1)
+        lx = matmul_toeplitz(self.col, x)
+        mx = np.zeros(self.n)
+        for inv in self.labels:
+            mx += np.bincount(inv, weights=x)[inv]
+        return lx - mx / self.s
+
+
+def error_matvec(sigma: float, deltas, us, n: int, x) -> np.ndarray:
+    """E x (see ErrorOperator)."""
+    return ErrorOperator(sigma, deltas, us, n).matvec(x)
 
 
 def error_spectral(sigma: float, deltas, us, n: int, dense_below: int = 2048, tol: float = 1e-12) -> float:
@@ -94,8 +105,8 @@ def error_spectral(sigma: float, deltas, us, n: int, dense_below: int = 2048, to
         return float(np.linalg.norm(error_dense(sigma, deltas, us, n), 2))
     from scipy.sparse.linalg import LinearOperator, eigsh
 
-    op = LinearOperator((n, n), matvec=lambda v: error_matvec(sigma, deltas, us, n, v.reshape(-1)),
-                        dtype=np.float64)
+    E = ErrorOperator(sigma, deltas, us, n)
+    op = LinearOperator((n, n), matvec=E.matvec, dtype=np.float64)
     vals = eigsh(op, k=1, which="LM", tol=tol, return_eigenvectors=False,
                  v0=np.random.default_rng(0).standard_normal(n))
     return float(np.abs(vals).max())

@@ -17,6 +17,10 @@ from ._binding import (  # noqa: F401
     bins_from_hashes,
     bins_layout,
     draw_hashes,
+    error_matvec,
+    error_norms,
+    error_rowmax,
+    error_workspace_bytes,
     fixed_blocks,
     raw,
     sample_bins,

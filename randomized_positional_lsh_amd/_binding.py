@@ -63,6 +63,12 @@ _SIGS = {
                                           _c_int, _c_int, _vp, _c_sz, _dp, _vp]),
     "plpsh_attention_fwd_literal": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                              _c_int, _c_int, _vp, _c_sz, _dp, _vp]),
+    "plpsh_error_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int]),
+    "plpsh_error_rowmax": (_c_int, [ctypes.c_double, _c_int, _c_int, _vp, _c_sz, _vp, _vp]),
+    "plpsh_error_matvec": (_c_int, [ctypes.c_double, _c_int, _c_int, _vp, _c_sz, _vp, _vp, _vp, _c_sz, _vp]),
+    "plpsh_error_norms": (_c_int, [ctypes.c_double, _c_int, _c_int, _dp, _dp, _c_int, ctypes.c_double,
+                                   ctypes.c_uint64, _vp, _c_sz, _dp, _dp, ctypes.POINTER(ctypes.c_int32),
+                                   ctypes.POINTER(ctypes.c_int32), _vp]),
     "plpsh_fixed_blocks_fwd": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                         ctypes.POINTER(ctypes.c_int32), _c_int, _vp, _c_sz, _vp]),
     "plpsh_alibi_dense_fwd": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
@@ -310,3 +316,63 @@ def alibi_dense(q, k, v, sigma, causal: bool = False, out=None, stream=None):
                                     _torch_dtype_code(q), _ptr(sig), int(bool(causal)), _stream(stream))
     _check(st, "plpsh_alibi_dense_fwd")
     return out
+
+
+# ------------------------------------------------- error of M~ against L* --
+
+def error_workspace_bytes(n: int, s: int, max_steps: int) -> int:
+    return int(_lib.plpsh_error_workspace_bytes(n, s, max_steps))
+
+
+def error_rowmax(sigma: float, bins: "Bins", out=None, stream=None):
+    """max_j |L*[r, j] - c[r, j] / s| for every row r (plpsh_error_rowmax);
+    ``bins`` must hold one head."""
+    import torch
+    if bins.heads != 1:
+        raise ValueError("error functions take the bins of one head")
+    out = torch.empty(bins.n, dtype=torch.float64, device=bins.buffer.device) if out is None else out
+    _check(_lib.plpsh_error_rowmax(float(sigma), bins.n, bins.s, ctypes.c_void_p(bins.buffer.data_ptr()),
+                                   bins.buffer.numel(), ctypes.c_void_p(out.data_ptr()), _stream(stream)),
+           "plpsh_error_rowmax")
+    return out
+
+
+def error_matvec(sigma: float, bins: "Bins", x, out=None, workspace=None, stream=None):
+    """(L* - M~) x for a float64 device vector x (plpsh_error_matvec)."""
+    import torch
+    if bins.heads != 1:
+        raise ValueError("error functions take the bins of one head")
+    if x.dtype != torch.float64 or x.numel() != bins.n or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float64 vector of length n")
+    out = torch.empty_like(x) if out is None else out
+    need = error_workspace_bytes(bins.n, bins.s, 0)
+    ws = torch.empty(need, dtype=torch.uint8, device=x.device) if workspace is None else workspace
+    _check(_lib.plpsh_error_matvec(float(sigma), bins.n, bins.s, ctypes.c_void_p(bins.buffer.data_ptr()),
+                                   bins.buffer.numel(), ctypes.c_void_p(x.data_ptr()),
+                                   ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                   _stream(stream)), "plpsh_error_matvec")
+    return out
+
+
+def error_norms(sigma: float, delta, u, n: int, max_steps: int = 300, tol: float = 1e-10, seed: int = 0,
+                device="cuda", workspace=None, stream=None) -> dict:
+    """||L* - M~||_2 and ||L* - M~||_max for one head's hashes
+    (plpsh_error_norms).  Returns spectral, maxnorm, argmax_row, steps."""
+    import torch
+    d = _f64(delta).reshape(-1)
+    uu = _f64(u).reshape(-1)
+    s = d.size
+    need = error_workspace_bytes(n, s, max_steps)
+    if need == 0:
+        raise ValueError("invalid sizes")
+    ws = torch.empty(need, dtype=torch.uint8, device=device) if workspace is None else workspace
+    spec = ctypes.c_double()
+    mx = ctypes.c_double()
+    row = ctypes.c_int32()
+    steps = ctypes.c_int32()
+    _check(_lib.plpsh_error_norms(float(sigma), n, s, _ptr(d), _ptr(uu), max_steps, float(tol),
+                                  ctypes.c_uint64(seed & (2 ** 64 - 1)), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                  ctypes.byref(spec), ctypes.byref(mx), ctypes.byref(row), ctypes.byref(steps),
+                                  _stream(stream)), "plpsh_error_norms")
+    return {"spectral": spec.value, "maxnorm": mx.value, "argmax_row": row.value, "steps": steps.value}
+

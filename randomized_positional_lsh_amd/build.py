@@ -29,6 +29,7 @@ COMMON = [
 SOURCES = {
     "bins.hip": ["-ffp-contract=off"],
     "attn.hip": [],
+    "errnorm.hip": [],
     "api.cpp": [],
     "sampler.cpp": ["-ffp-contract=off"],
 }

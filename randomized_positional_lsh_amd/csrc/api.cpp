@@ -159,6 +159,86 @@ plpsh_status attention_common(const void* q, const void* k, const void* v, void*
   return attention_on_bins(q, k, v, o, batch, hq, hkv, n, d, dtype, delta, s, causal, ws, st);
 }
 
+// ---- error of the mask mean against L* (Theorem 2.1), large n
+
+constexpr int kMaxLanczos = 1000;
+
+bool valid_err(double sigma, int n, int s) {
+  return std::isfinite(sigma) && sigma > 0.0 && n >= 1 && n <= PLPSH_MAX_N && s >= 1 && s <= PLPSH_MAX_S;
+}
+
+// Number of eigenvalues below x of the symmetric tridiagonal matrix with
+// diagonal a[0..k) and off-diagonal b[0..k-1) (Sturm sequence of the LDL^T
+// pivots).
+int sturm_below(const std::vector<double>& a, const std::vector<double>& b, int k, double x) {
+  int cnt = 0;
+  double q = 1.0;
+  for (int i = 0; i < k; ++i) {
+    const double bb = i > 0 ? b[i - 1] * b[i - 1] : 0.0;
+    q = a[i] - x - (i > 0 ? bb / q : 0.0);
+    if (q == 0.0) q = -1e-300;
+    cnt += q < 0.0;
+  }
+  return cnt;
+}
+
+// Largest |eigenvalue| of that matrix, by bisection on the Sturm count.
+double tridiag_spectral(const std::vector<double>& a, const std::vector<double>& b, int k) {
+  double R = 0.0;
+  for (int i = 0; i < k; ++i)
+    R = std::max(R, std::fabs(a[i]) + (i > 0 ? std::fabs(b[i - 1]) : 0.0) + (i + 1 < k ? std::fabs(b[i]) : 0.0));
+  if (R == 0.0) return 0.0;
+  double lo = -R, hi = R;  // largest eigenvalue: count(x) == k for x above it
+  for (int it = 0; it < 200 && hi - lo > 1e-15 * R; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    (sturm_below(a, b, k, mid) < k ? lo : hi) = mid;
+  }
+  const double lmax = 0.5 * (lo + hi);
+  lo = -R;
+  hi = R;  // smallest eigenvalue: count(x) >= 1 for x above it
+  for (int it = 0; it < 200 && hi - lo > 1e-15 * R; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    (sturm_below(a, b, k, mid) >= 1 ? hi : lo) = mid;
+  }
+  const double lmin = 0.5 * (lo + hi);
+  return std::max(std::fabs(lmax), std::fabs(lmin));
+}
+
+struct ErrWorkspace {
+  size_t bins, scan, V, w, rowmax, h, part_v, part_i, scal, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+ErrWorkspace err_workspace(int n, int s, int max_steps) {
+  ErrWorkspace L{};
+  size_t o = 0;
+  L.bins = o;
+  o = align256(o + plpsh::bins_layout(1, s, n).total);
+  L.scan = o;
+  o = align256(o + plpsh::err_scan_bytes(n));
+  L.V = o;
+  o = align256(o + static_cast<size_t>(max_steps + 1) * n * sizeof(double));
+  L.w = o;
+  o = align256(o + static_cast<size_t>(n) * sizeof(double));
+  L.rowmax = o;
+  o = align256(o + static_cast<size_t>(n) * sizeof(double));
+  L.h = o;
+  o = align256(o + 2 * static_cast<size_t>(max_steps + 1) * sizeof(double));
+  L.part_v = o;
+  o = align256(o + 256 * sizeof(double));
+  L.part_i = o;
+  o = align256(o + 256 * sizeof(int));
+  L.scal = o;
+  o = align256(o + 8 * sizeof(double));
+  L.total = o;
+  return L;
+}
+
+const plpsh::PlanRec* plan_of(const void* bins, int s, int n) {
+  return reinterpret_cast<const plpsh::PlanRec*>(static_cast<const char*>(bins) + plpsh::bins_layout(1, s, n).off_plan);
+}
+
 }  // namespace
 
 extern "C" {
@@ -327,6 +407,130 @@ plpsh_status plpsh_alibi_dense_fwd(const void* q, const void* k, const void* v, 
                                          static_cast<hipStream_t>(stream)),
                  "dense ALiBi kernel launch"))
     return PLPSH_ERR_HIP;
+  return PLPSH_OK;
+}
+
+size_t plpsh_error_workspace_bytes(int32_t n, int32_t s, int32_t max_steps) {
+  if (!valid_err(1.0, n, s) || max_steps < 0 || max_steps > kMaxLanczos) return 0;
+  if (max_steps == 0) return plpsh::err_scan_bytes(n);
+  return err_workspace(n, s, max_steps).total;
+}
+
+plpsh_status plpsh_error_rowmax(double sigma, int32_t n, int32_t s, const void* bins, size_t bins_bytes,
+                                double* rowmax, void* stream) {
+  if (!valid_err(sigma, n, s) || !bins || !rowmax || (reinterpret_cast<uintptr_t>(bins) & 255))
+    return PLPSH_ERR_INVALID_ARGUMENT;
+  if (bins_bytes < plpsh::bins_layout(1, s, n).total) return PLPSH_ERR_WORKSPACE_TOO_SMALL;
+  if (hip_failed(plpsh::launch_err_rowmax(plan_of(bins, s, n), n, s, sigma, rowmax, static_cast<hipStream_t>(stream)),
+                 "error row-maximum kernel launch"))
+    return PLPSH_ERR_HIP;
+  return PLPSH_OK;
+}
+
+plpsh_status plpsh_error_matvec(double sigma, int32_t n, int32_t s, const void* bins, size_t bins_bytes,
+                                const double* x, double* y, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_err(sigma, n, s) || !bins || !x || !y || !workspace || (reinterpret_cast<uintptr_t>(bins) & 255) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255) || x == y)
+    return PLPSH_ERR_INVALID_ARGUMENT;
+  if (bins_bytes < plpsh::bins_layout(1, s, n).total || workspace_bytes < plpsh::err_scan_bytes(n))
+    return PLPSH_ERR_WORKSPACE_TOO_SMALL;
+  if (hip_failed(plpsh::launch_err_matvec(plan_of(bins, s, n), n, s, sigma, x, y, workspace,
+                                          static_cast<hipStream_t>(stream)),
+                 "error product kernels launch"))
+    return PLPSH_ERR_HIP;
+  return PLPSH_OK;
+}
+
+plpsh_status plpsh_error_norms(double sigma, int32_t n, int32_t s, const double* delta, const double* u,
+                               int32_t max_steps, double tol, uint64_t seed, void* workspace, size_t workspace_bytes,
+                               double* spectral, double* maxnorm, int32_t* argmax_row, int32_t* steps,
+                               void* stream) {
+  if (!valid_err(sigma, n, s) || !valid_hashes(delta, u, s) || max_steps < 1 || max_steps > kMaxLanczos ||
+      !(tol > 0.0) || !workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) || !spectral || !maxnorm)
+    return PLPSH_ERR_INVALID_ARGUMENT;
+  const ErrWorkspace L = err_workspace(n, s, max_steps);
+  if (workspace_bytes < L.total) return PLPSH_ERR_WORKSPACE_TOO_SMALL;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  void* bins = ws + L.bins;
+  plpsh_status r = run_bins(1, s, n, delta, u, bins, st);
+  if (r != PLPSH_OK) return r;
+  const plpsh::PlanRec* plan = plan_of(bins, s, n);
+  double* V = reinterpret_cast<double*>(ws + L.V);
+  double* w = reinterpret_cast<double*>(ws + L.w);
+  double* rowmax = reinterpret_cast<double*>(ws + L.rowmax);
+  double* h1 = reinterpret_cast<double*>(ws + L.h);
+  double* h2 = h1 + (max_steps + 1);
+  double* scal = reinterpret_cast<double*>(ws + L.scal);
+  const size_t ld = static_cast<size_t>(n);
+
+  // max norm: row maxima, then the largest of them
+  if (hip_failed(plpsh::launch_err_rowmax(plan, n, s, sigma, rowmax, st), "error row-maximum kernel launch") ||
+      hip_failed(plpsh::launch_err_argmax(rowmax, n, reinterpret_cast<double*>(ws + L.part_v),
+                                          reinterpret_cast<int*>(ws + L.part_i), scal + 4,
+                                          reinterpret_cast<int*>(scal + 5), st),
+                 "argmax kernel launch"))
+    return PLPSH_ERR_HIP;
+
+  // spectral norm: Lanczos on the symmetric E with full reorthogonalisation
+  // (classical Gram-Schmidt, twice); the extreme eigenvalues of the
+  // tridiagonal matrix by bisection after every step
+  std::vector<double> v0(n);
+  {
+    uint64_t state = seed;
+    double nrm = 0.0;
+    for (int i = 0; i < n; ++i) {
+      state += 0x9E3779B97F4A7C15ull;
+      uint64_t z = state;
+      z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+      z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+      z ^= z >> 31;
+      v0[i] = static_cast<double>(z >> 11) * 0x1p-53 - 0.5;
+      nrm += v0[i] * v0[i];
+    }
+    nrm = std::sqrt(nrm);
+    for (double& x : v0) x /= nrm;
+  }
+  if (hip_failed(hipMemcpyAsync(V, v0.data(), n * sizeof(double), hipMemcpyHostToDevice, st), "hipMemcpyAsync(v0)") ||
+      hip_failed(hipStreamSynchronize(st), "hipStreamSynchronize"))
+    return PLPSH_ERR_HIP;
+  std::vector<double> alpha, beta;
+  double spec = 0.0, prev = -1.0;
+  int stable = 0, k = 0;
+  double host[8];
+  for (k = 0; k < max_steps; ++k) {
+    double* vk = V + k * ld;
+    bool fail = hip_failed(plpsh::launch_err_matvec(plan, n, s, sigma, vk, w, ws + L.scan, st), "error product");
+    fail = fail || hip_failed(plpsh::launch_err_dots(V, ld, k + 1, w, n, h1, st), "dots") ||
+           hip_failed(plpsh::launch_err_sub_proj(V, ld, h1, k + 1, n, w, st), "projection") ||
+           hip_failed(plpsh::launch_err_dots(V, ld, k + 1, w, n, h2, st), "dots") ||
+           hip_failed(plpsh::launch_err_sub_proj(V, ld, h2, k + 1, n, w, st), "projection") ||
+           hip_failed(plpsh::launch_err_dots(w, ld, 1, w, n, scal + 2, st), "norm") ||
+           hip_failed(hipMemcpyAsync(scal, h1 + k, sizeof(double), hipMemcpyDeviceToDevice, st), "copy") ||
+           hip_failed(hipMemcpyAsync(scal + 1, h2 + k, sizeof(double), hipMemcpyDeviceToDevice, st), "copy") ||
+           hip_failed(hipMemcpyAsync(host, scal, 8 * sizeof(double), hipMemcpyDeviceToHost, st), "copy") ||
+           hip_failed(hipStreamSynchronize(st), "hipStreamSynchronize");
+    if (fail) return PLPSH_ERR_HIP;
+    alpha.push_back(host[0] + host[1]);
+    const double bk = std::sqrt(std::max(host[2], 0.0));
+    spec = tridiag_spectral(alpha, beta, k + 1);
+    if (k == 0) {
+      *maxnorm = host[4];
+      int im = 0;
+      std::memcpy(&im, &host[5], sizeof(int));
+      if (argmax_row) *argmax_row = im;
+    }
+    stable = (prev >= 0.0 && std::fabs(spec - prev) <= tol * spec) ? stable + 1 : 0;
+    prev = spec;
+    if (stable >= 3 || bk <= 1e-13 * std::max(spec, 1e-300) || k + 1 == max_steps || k + 1 == n) {
+      ++k;
+      break;
+    }
+    beta.push_back(bk);
+    if (hip_failed(plpsh::launch_err_scale(w, 1.0 / bk, n, V + (k + 1) * ld, st), "scale")) return PLPSH_ERR_HIP;
+  }
+  *spectral = spec;
+  if (steps) *steps = k;
   return PLPSH_OK;
 }
 

@@ -38,4 +38,15 @@ hipError_t launch_alibi_fwd(const void* q, const void* k, const void* v, void* o
                             int batch, int hq, int hkv, int n, int d, int dtype,
                             const float* beta_host, int causal, hipStream_t st);
 
+// Error of the mask mean against L* (errnorm.hip).  `plan` is the plan-record
+// array of one head; scratch for the products is err_scan_bytes(n) bytes.
+size_t err_scan_bytes(int n);
+hipError_t launch_err_rowmax(const PlanRec* plan, int n, int s, double sigma, double* rowmax, hipStream_t st);
+hipError_t launch_err_matvec(const PlanRec* plan, int n, int s, double sigma, const double* x, double* y,
+                             void* scratch, hipStream_t st);
+hipError_t launch_err_dots(const double* V, size_t ld, int m, const double* w, int n, double* out, hipStream_t st);
+hipError_t launch_err_sub_proj(const double* V, size_t ld, const double* h, int m, int n, double* w, hipStream_t st);
+hipError_t launch_err_scale(const double* w, double c, int n, double* v, hipStream_t st);
+hipError_t launch_err_argmax(const double* a, int n, double* pv, int* pi, double* out_v, int* out_i, hipStream_t st);
+
 }  // namespace plpsh

@@ -149,6 +149,39 @@ def test_fixed_blocks_validation():
     assert st == B.WORKSPACE_TOO_SMALL
 
 
+def test_error_functions_validation():
+    lib = B.raw()
+    dl = np.array([4.0, 9.0])
+    uu = np.array([1.0, 0.0])
+    # workspace sizes: invalid sizes give 0; products need the scan scratch
+    assert lib.plpsh_error_workspace_bytes(0, 2, 0) == 0
+    assert lib.plpsh_error_workspace_bytes(100, 0, 0) == 0
+    assert lib.plpsh_error_workspace_bytes(100, 2, 1001) == 0
+    assert lib.plpsh_error_workspace_bytes(100, 2, 0) > 0
+    assert lib.plpsh_error_workspace_bytes(100, 2, 10) > lib.plpsh_error_workspace_bytes(100, 2, 0)
+    for sigma, n, s in [(0.0, 64, 2), (float("nan"), 64, 2), (-1.0, 64, 2), (4.0, 0, 2), (4.0, 64, 0),
+                        (4.0, B.MAX_N + 1, 2), (4.0, 64, B.MAX_S + 1)]:
+        assert lib.plpsh_error_rowmax(sigma, n, s, FAKE, 1 << 30, FAKE, None) == B.INVALID_ARGUMENT
+        assert lib.plpsh_error_matvec(sigma, n, s, FAKE, 1 << 30, FAKE, ctypes.c_void_p((1 << 21)), FAKE, 1 << 30,
+                                      None) == B.INVALID_ARGUMENT
+    assert lib.plpsh_error_rowmax(4.0, 64, 2, FAKE, 10, FAKE, None) == B.WORKSPACE_TOO_SMALL
+    assert lib.plpsh_error_matvec(4.0, 64, 2, FAKE, 1 << 30, FAKE, FAKE, FAKE, 1 << 30, None) == B.INVALID_ARGUMENT
+    assert lib.plpsh_error_matvec(4.0, 64, 2, FAKE, 1 << 30, FAKE, ctypes.c_void_p(1 << 21), FAKE, 10,
+                                  None) == B.WORKSPACE_TOO_SMALL
+    out = ctypes.c_double()
+    i32 = ctypes.c_int32()
+    args = lambda **kw: dict(dict(sigma=4.0, n=64, s=2, d=B._ptr(dl), u=B._ptr(uu), steps=20, tol=1e-10,
+                                  ws=FAKE, wsb=1 << 30), **kw)
+    call = lambda a: lib.plpsh_error_norms(a["sigma"], a["n"], a["s"], a["d"], a["u"], a["steps"], a["tol"], 0,
+                                           a["ws"], a["wsb"], ctypes.byref(out), ctypes.byref(out),
+                                           ctypes.byref(i32), ctypes.byref(i32), None)
+    bad_u = np.array([5.0, 0.0])
+    for kw in [dict(steps=0), dict(steps=1001), dict(tol=0.0), dict(d=None), dict(u=B._ptr(bad_u)),
+               dict(ws=None), dict(ws=ctypes.c_void_p((1 << 20) + 8)), dict(sigma=0.0)]:
+        assert call(args(**kw)) == B.INVALID_ARGUMENT, kw
+    assert call(args(wsb=100)) == B.WORKSPACE_TOO_SMALL
+
+
 def test_draw_validation():
     lib = B.raw()
     sig = np.array([1.0])
