@@ -22,7 +22,8 @@ and Japanese with the same section structure:
 * [P, Key results]     O(1/sqrt(s)) error decay; experiments
 * [P, Limitations]     no wall-clock claim against dense kernels
 
-``oracle.convergence`` gives the error E = L* - M~ of [P, Theorem 2.1] at
+``oracle.grad`` gives the row normalisers and the gradients of T~ for
+training with the approximation.  ``oracle.convergence`` gives the error E = L* - M~ of [P, Theorem 2.1] at
 sequence lengths where dense matrices no longer fit (row maxima, products
 E x, spectral norm).
 
@@ -48,6 +49,7 @@ from .plsh import (  # noqa: F401
     support_interval,
 )
 from .sampler import splitmix64, sample_hashes  # noqa: F401
+from .grad import plsh_attention_grad, plsh_attention_lse  # noqa: F401
 from .convergence import (  # noqa: F401
     error_dense,
     error_matvec,

@@ -509,3 +509,54 @@ def test_p13_closed_forms():
     bound = 2 * rho / (1 - rho)
     spec = oracle.error_spectral(sigma, [0.5], [0.0], n)      # ARPACK path (n >= 2048)
     assert 0.999 * bound < spec < bound
+
+
+# ---------------------------------------------------------------- P14 ------
+# [P, Key results, experimental validation]: training with T~ needs its
+# gradients and the row normalisers.  Pinned by central finite differences
+# of the forward oracle and by the one-block case.
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_p14_gradients_match_finite_differences(causal):
+    rng = _rng(31)
+    B, Hq, Hkv, n, d = 1, 2, 1, 11, 4
+    q = rng.standard_normal((B, Hq, n, d))
+    k = rng.standard_normal((B, Hkv, n, d))
+    v = rng.standard_normal((B, Hkv, n, d))
+    do = rng.standard_normal((B, Hq, n, d))
+    dl = np.stack([_draw(rng, 3.0, 4)[0] for _ in range(Hq)])
+    uu = dl * rng.uniform(0, 1, dl.shape)
+    dq, dk, dv = oracle.plsh_attention_grad(q, k, v, do, dl, uu, causal)
+    f = lambda q_, k_, v_: float((do * oracle.plsh_attention(q_, k_, v_, dl, uu, causal)).sum())
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in [(0, 0, 0, 0), (0, 0, 5, 2), (0, x.shape[1] - 1, n - 1, 3), (0, x.shape[1] - 1, 3, 1)]:
+            xp = x.copy()
+            xm = x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = {"q": q, "k": k, "v": v}
+            args_p[name] = xp
+            args_m[name] = xm
+            fd = (f(args_p["q"], args_p["k"], args_p["v"]) - f(args_m["q"], args_m["k"], args_m["v"])) / (2 * eps)
+            assert abs(fd - g[idx]) <= 1e-7 * max(1.0, abs(fd)), (name, idx, fd, g[idx])
+
+
+def test_p14_lse_one_block_is_logsumexp():
+    """One block over everything: c = s everywhere, so the normaliser is
+    log s + logsumexp of the scaled logits (SciPy)."""
+    from scipy.special import logsumexp
+    rng = _rng(32)
+    B, H, n, d, s = 2, 2, 40, 8, 3
+    q = rng.standard_normal((B, H, n, d))
+    k = rng.standard_normal((B, H, n, d))
+    dl = np.full((H, s), 10.0 * n)
+    uu = np.zeros((H, s))
+    got = oracle.plsh_attention_lse(q, k, k, dl, uu, False)
+    S = np.einsum("bhrd,bhjd->bhrj", q, k) / math.sqrt(d)
+    assert np.allclose(got, math.log(s) + logsumexp(S, axis=-1), rtol=0, atol=1e-12)
+    # causal: row r sums over j <= r
+    got = oracle.plsh_attention_lse(q, k, k, dl, uu, True)
+    Sc = np.where(np.tril(np.ones((n, n), bool)), S, -np.inf)
+    assert np.allclose(got, math.log(s) + logsumexp(Sc, axis=-1), rtol=0, atol=1e-12)
