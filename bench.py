@@ -19,6 +19,11 @@ Prints ONE JSON line.  Besides the contract fields it carries:
   literal      : the same step with the attention computed as one short
                  attention per hash (plpsh_attention_fwd_literal, the
                  reduction of Theorem 2.2 taken literally), same bins
+  backward     : a training step's attention on the same bins: the forward
+                 with row normalisers (plpsh_attention_fwd_lse) and the
+                 backward pass (plpsh_attention_bwd), each timed with HIP
+                 events; useful MFMA rate of the backward (5 products per
+                 counted pair against the forward's 2)
   fixed_blocks : the deterministic fixed-blocks baseline (plpsh_fixed_blocks_fwd,
                  block b_h = round(2 sigma_h), the mean of Gamma(2, sigma_h))
   crossover    : PLSH vs dense ALiBi step times over n (Mistral shape)
@@ -228,6 +233,40 @@ def literal(run, steps=10, warmup=3):
     return a.elapsed_time(b) / steps
 
 
+def backward(P, W, run, flops_fwd, steps=10, warmup=3):
+    import numpy as np
+    import torch
+    q, k, v = run.q, run.k, run.v
+    bins = P.Bins(run.ws, W.heads_q, W.s, W.n)
+    delta = run.delta.reshape(W.heads_q, W.s)
+    gen = torch.Generator(device=q.device)
+    gen.manual_seed(9)
+    do = torch.randn(q.shape, generator=gen, device=q.device, dtype=torch.float32).to(q.dtype)
+    o = torch.empty_like(q)
+    lse = torch.empty((W.batch, W.heads_q, W.n), dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(P.raw().plpsh_attention_bwd_workspace_bytes(W.batch, W.heads_q, W.n), dtype=torch.uint8,
+                     device=q.device)
+    for _ in range(warmup):
+        P.attention_lse(q, k, v, bins, causal=W.causal, delta=delta, out=o, lse=lse)
+        P.attention_bwd(q, k, v, o, do, lse, bins, causal=W.causal, delta=delta, dq=dq, dk=dk, dv=dv, workspace=ws)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for a, b, c in ev:
+        a.record()
+        P.attention_lse(q, k, v, bins, causal=W.causal, delta=delta, out=o, lse=lse)
+        b.record()
+        P.attention_bwd(q, k, v, o, do, lse, bins, causal=W.causal, delta=delta, dq=dq, dk=dk, dv=dv, workspace=ws)
+        c.record()
+    torch.cuda.synchronize()
+    f_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    b_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    tflops = 2.5 * flops_fwd / (b_ms * 1e-3) / 1e12
+    return {"fwd_lse_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4), "bwd_over_fwd": round(b_ms / f_ms, 2),
+            "train_tokens_per_s": round(W.batch * W.n / ((f_ms + b_ms) * 1e-3), 1),
+            "bwd_useful_tflops": round(tflops, 2), "bwd_mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 def fixed_blocks(P, W, q, k, v, steps=10, warmup=3):
     import numpy as np
     import torch
@@ -386,6 +425,9 @@ def main():
                    "sigma": "2^(8(h+1)/H)", "parallelism": "single GPU"},
         "roofline": roofline,
     }
+    if W.dtype == "bf16":
+        line["backward"] = backward(P, W, run, flops)
+        log(f"backward {line['backward']}")
     lms = literal(run)
     line["literal"] = {"kernel_ms": round(lms, 4), "fused_kernel_ms": round(kern_ms, 4),
                        "slowdown_vs_fused": round(lms / kern_ms, 2)}

@@ -264,6 +264,50 @@ plpsh_status plpsh_attention_fwd_literal(const void* q, const void* k, const voi
                                          size_t bins_bytes, const double* delta, void* stream);
 
 /*
+ * plpsh_attention_fwd_lse -- plpsh_attention_fwd_bins that also writes each
+ * row's log-normaliser, for the backward pass:
+ *   lse[b, h, r] = log sum_j c[r, j] C[r, j] exp(S[r, j])   (natural log)
+ * lse: device, float32 [batch, heads_q, n], caller-owned.  The weights of T~
+ * are then P[r, j] = c[r, j] C[r, j] exp(S[r, j] - lse[r]).  Other arguments,
+ * layouts and errors as plpsh_attention_fwd_bins.
+ */
+plpsh_status plpsh_attention_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                                     int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                     int32_t n, int32_t head_dim, plpsh_dtype dtype,
+                                     int32_t s, int32_t causal, const void* bins,
+                                     size_t bins_bytes, const double* delta, void* stream);
+
+/* Workspace of plpsh_attention_bwd: batch * heads_q * n floats, 256-byte
+ * rounded (0 for invalid sizes). */
+size_t plpsh_attention_bwd_workspace_bytes(int32_t batch, int32_t heads_q, int32_t n);
+
+/*
+ * plpsh_attention_bwd -- gradients of sum(dO o T~) for training with the
+ * approximation (the pages train and fine-tune models with it: Key results,
+ * experimental validation).  With P as above and the counts c of the same
+ * bins (which do not depend on Q, K, V):
+ *   dV = P^T dO,  dS = P o (dO V^T - D),  D_r = <dO_r, O_r>,
+ *   dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d),
+ * with the gradients of the query heads of a KV group summed into its KV
+ * head.
+ *   q, k, v, o : the forward inputs and output (o from the same bins);
+ *   dout       : dO, layout of o;   lse: from plpsh_attention_fwd_lse;
+ *   dq         : device out, layout of q;  dk, dv: device out, layout of k
+ *                (every element written; no accumulation into them);
+ *   bins, delta: as plpsh_attention_fwd_bins (delta only orders the work);
+ *   workspace  : device, 256-byte aligned, >=
+ *                plpsh_attention_bwd_workspace_bytes(batch, heads_q, n).
+ * bf16 only (PLPSH_ERR_UNSUPPORTED for f32); head_dim 64 or 128.  Arithmetic:
+ * bf16 products on the matrix cores with fp32 accumulation; P and dS are
+ * rounded to bf16 before their products.  Asynchronous on `stream`.
+ */
+plpsh_status plpsh_attention_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                 const float* lse, void* dq, void* dk, void* dv, int32_t batch, int32_t heads_q,
+                                 int32_t heads_kv, int32_t n, int32_t head_dim, plpsh_dtype dtype, int32_t s,
+                                 int32_t causal, const void* bins, size_t bins_bytes, const double* delta,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * plpsh_alibi_dense_fwd -- exact ALiBi attention T* (the quantity the
  * approximation targets, Methodology 1), dense over all keys:
  *   O_r = sum_j C[r,j] exp(S[r,j] - |r-j|/sigma_h) v_j / sum_j (same weights)

@@ -11,8 +11,10 @@ from ._binding import (  # noqa: F401
     PlpshError,
     alibi_dense,
     attention,
+    attention_bwd,
     attention_from_bins,
     attention_literal,
+    attention_lse,
     attention_hashes,
     bins_from_hashes,
     bins_layout,

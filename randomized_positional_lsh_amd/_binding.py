@@ -63,6 +63,11 @@ _SIGS = {
                                           _c_int, _c_int, _vp, _c_sz, _dp, _vp]),
     "plpsh_attention_fwd_literal": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                              _c_int, _c_int, _vp, _c_sz, _dp, _vp]),
+    "plpsh_attention_fwd_lse": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                         _c_int, _c_int, _vp, _c_sz, _dp, _vp]),
+    "plpsh_attention_bwd_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int]),
+    "plpsh_attention_bwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
+                                     _c_int, _c_int, _c_int, _c_int, _vp, _c_sz, _dp, _vp, _c_sz, _vp]),
     "plpsh_error_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int]),
     "plpsh_error_rowmax": (_c_int, [ctypes.c_double, _c_int, _c_int, _vp, _c_sz, _vp, _vp]),
     "plpsh_error_matvec": (_c_int, [ctypes.c_double, _c_int, _c_int, _vp, _c_sz, _vp, _vp, _vp, _c_sz, _vp]),
@@ -301,6 +306,47 @@ def attention_literal(q, k, v, bins: "Bins", causal: bool = False, delta=None, o
     (plpsh_attention_fwd_literal)."""
     return _on_bins(_lib.plpsh_attention_fwd_literal, "plpsh_attention_fwd_literal", q, k, v, bins, causal, delta,
                     out, stream)
+
+
+def attention_lse(q, k, v, bins: "Bins", causal: bool = False, delta=None, out=None, lse=None, stream=None):
+    """Forward on a bin buffer that also returns each row's log-normaliser
+    (plpsh_attention_fwd_lse): (out, lse) with lse float32 [B, Hq, n]."""
+    import torch
+    B, Hq, Hkv, n, d = _qkv_shapes(q, k, v)
+    if bins.heads != Hq or bins.n != n:
+        raise ValueError("bins were computed for other sizes")
+    dl = None if delta is None else _f64(delta)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = _lib.plpsh_attention_fwd_lse(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                      ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                      ctypes.c_void_p(lse.data_ptr()), B, Hq, Hkv, n, d, _torch_dtype_code(q), bins.s,
+                                      int(bool(causal)), ctypes.c_void_p(bins.buffer.data_ptr()), bins.buffer.numel(),
+                                      None if dl is None else _ptr(dl), _stream(stream))
+    _check(st, "plpsh_attention_fwd_lse")
+    return out, lse
+
+
+def attention_bwd(q, k, v, out, dout, lse, bins: "Bins", causal: bool = False, delta=None, dq=None, dk=None,
+                  dv=None, workspace=None, stream=None):
+    """(dq, dk, dv) of sum(dout * T~) (plpsh_attention_bwd); bf16 only."""
+    import torch
+    B, Hq, Hkv, n, d = _qkv_shapes(q, k, v)
+    if bins.heads != Hq or bins.n != n:
+        raise ValueError("bins were computed for other sizes")
+    dl = None if delta is None else _f64(delta)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = int(_lib.plpsh_attention_bwd_workspace_bytes(B, Hq, n))
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = _lib.plpsh_attention_bwd(ptr(q), ptr(k), ptr(v), ptr(out), ptr(dout), ptr(lse), ptr(dq), ptr(dk), ptr(dv),
+                                  B, Hq, Hkv, n, d, _torch_dtype_code(q), bins.s, int(bool(causal)),
+                                  ptr(bins.buffer), bins.buffer.numel(), None if dl is None else _ptr(dl), ptr(ws),
+                                  ws.numel(), _stream(stream))
+    _check(st, "plpsh_attention_bwd")
+    return dq, dk, dv
 
 
 def alibi_dense(q, k, v, sigma, causal: bool = False, out=None, stream=None):

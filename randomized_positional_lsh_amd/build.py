@@ -30,6 +30,7 @@ SOURCES = {
     "bins.hip": ["-ffp-contract=off"],
     "attn.hip": [],
     "errnorm.hip": [],
+    "bwd.hip": [],
     "api.cpp": [],
     "sampler.cpp": ["-ffp-contract=off"],
 }

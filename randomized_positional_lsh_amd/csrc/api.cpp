@@ -133,7 +133,7 @@ plpsh_status check_qkv(const void* q, const void* k, const void* v, void* o, int
 // widest bins (largest key windows) are scheduled first when delta is known.
 plpsh_status attention_on_bins(const void* q, const void* k, const void* v, void* o, int batch, int hq, int hkv,
                                int n, int d, int dtype, const double* delta, int s, int causal, const void* bins,
-                               hipStream_t st, bool literal = false) {
+                               hipStream_t st, bool literal = false, float* lse = nullptr) {
   std::vector<uint16_t> order(hq);
   std::iota(order.begin(), order.end(), 0);
   if (delta) {
@@ -143,7 +143,7 @@ plpsh_status attention_on_bins(const void* q, const void* k, const void* v, void
     std::stable_sort(order.begin(), order.end(), [&](uint16_t a, uint16_t b) { return cost[a] > cost[b]; });
   }
   if (hip_failed(plpsh::launch_plsh_fwd(q, k, v, o, batch, hq, hkv, n, d, dtype, s, causal, bins, order.data(),
-                                        literal, st),
+                                        literal, lse, st),
                  "attention kernel launch"))
     return PLPSH_ERR_HIP;
   return PLPSH_OK;
@@ -361,7 +361,8 @@ plpsh_status plpsh_fixed_blocks_fwd(const void* q, const void* k, const void* v,
 namespace {
 plpsh_status fwd_bins(const void* q, const void* k, const void* v, void* o, int32_t batch, int32_t heads_q,
                       int32_t heads_kv, int32_t n, int32_t head_dim, plpsh_dtype dtype, int32_t s, int32_t causal,
-                      const void* bins, size_t bins_bytes, const double* delta, void* stream, bool literal) {
+                      const void* bins, size_t bins_bytes, const double* delta, void* stream, bool literal,
+                      float* lse = nullptr) {
   plpsh_status r = check_qkv(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, causal);
   if (r != PLPSH_OK) return r;
   if (!valid_hs(heads_q, s)) return PLPSH_ERR_INVALID_ARGUMENT;
@@ -373,9 +374,18 @@ plpsh_status fwd_bins(const void* q, const void* k, const void* v, void* o, int3
       if (!finite_pos(delta[i])) return PLPSH_ERR_INVALID_ARGUMENT;
   }
   return attention_on_bins(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, delta, s, causal, bins,
-                           static_cast<hipStream_t>(stream), literal);
+                           static_cast<hipStream_t>(stream), literal, lse);
 }
 }  // namespace
+
+plpsh_status plpsh_attention_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse, int32_t batch,
+                                     int32_t heads_q, int32_t heads_kv, int32_t n, int32_t head_dim,
+                                     plpsh_dtype dtype, int32_t s, int32_t causal, const void* bins,
+                                     size_t bins_bytes, const double* delta, void* stream) {
+  if (!lse && batch > 0 && n > 0) return PLPSH_ERR_INVALID_ARGUMENT;
+  return fwd_bins(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, s, causal, bins, bins_bytes, delta,
+                  stream, false, lse);
+}
 
 plpsh_status plpsh_attention_fwd_bins(const void* q, const void* k, const void* v, void* o, int32_t batch,
                                       int32_t heads_q, int32_t heads_kv, int32_t n, int32_t head_dim,
@@ -534,4 +544,52 @@ plpsh_status plpsh_error_norms(double sigma, int32_t n, int32_t s, const double*
   return PLPSH_OK;
 }
 
+size_t plpsh_attention_bwd_workspace_bytes(int32_t batch, int32_t heads_q, int32_t n) {
+  if (batch < 0 || heads_q < 1 || n < 0 || n > PLPSH_MAX_N) return 0;
+  return std::max<size_t>(256, (static_cast<size_t>(batch) * heads_q * n * sizeof(float) + 255) & ~size_t{255});
+}
+
+plpsh_status plpsh_attention_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                 const float* lse, void* dq, void* dk, void* dv, int32_t batch, int32_t heads_q,
+                                 int32_t heads_kv, int32_t n, int32_t head_dim, plpsh_dtype dtype, int32_t s,
+                                 int32_t causal, const void* bins, size_t bins_bytes, const double* delta,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  plpsh_status r = check_qkv(q, k, v, dq, batch, heads_q, heads_kv, n, head_dim, dtype, causal);
+  if (r != PLPSH_OK) return r;
+  if (!valid_hs(heads_q, s)) return PLPSH_ERR_INVALID_ARGUMENT;
+  if (batch == 0 || n == 0) return PLPSH_OK;
+  if (!o || !dout || !lse || !dk || !dv || !workspace || (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return PLPSH_ERR_INVALID_ARGUMENT;
+  for (const void* p : {o, dout, static_cast<const void*>(dk), static_cast<const void*>(dv)})
+    if (reinterpret_cast<uintptr_t>(p) & 15) return PLPSH_ERR_INVALID_ARGUMENT;
+  if (dtype != PLPSH_DTYPE_BF16) return PLPSH_ERR_UNSUPPORTED;
+  if (!bins || (reinterpret_cast<uintptr_t>(bins) & 255)) return PLPSH_ERR_INVALID_ARGUMENT;
+  if (bins_bytes < plpsh::bins_layout(heads_q, s, n).total) return PLPSH_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace_bytes < plpsh_attention_bwd_workspace_bytes(batch, heads_q, n)) return PLPSH_ERR_WORKSPACE_TOO_SMALL;
+  if (delta) {
+    for (long long i = 0; i < static_cast<long long>(heads_q) * s; ++i)
+      if (!finite_pos(delta[i])) return PLPSH_ERR_INVALID_ARGUMENT;
+  }
+  // heads (dQ) and KV groups (dK, dV) with the widest bins first
+  std::vector<double> cost(heads_q, 0.0);
+  if (delta)
+    for (int h = 0; h < heads_q; ++h)
+      for (int i = 0; i < s; ++i) cost[h] += std::min(delta[h * s + i], static_cast<double>(n));
+  std::vector<uint16_t> oq(heads_q), okv(heads_kv);
+  std::iota(oq.begin(), oq.end(), 0);
+  std::iota(okv.begin(), okv.end(), 0);
+  std::stable_sort(oq.begin(), oq.end(), [&](uint16_t a, uint16_t b) { return cost[a] > cost[b]; });
+  const int grp = heads_q / heads_kv;
+  std::vector<double> gcost(heads_kv, 0.0);
+  for (int h = 0; h < heads_q; ++h) gcost[h / grp] += cost[h];
+  std::stable_sort(okv.begin(), okv.end(), [&](uint16_t a, uint16_t b) { return gcost[a] > gcost[b]; });
+  if (hip_failed(plpsh::launch_plsh_bwd(q, k, v, o, dout, lse, dq, dk, dv, batch, heads_q, heads_kv, n, head_dim, s,
+                                        causal, bins, oq.data(), okv.data(), static_cast<float*>(workspace),
+                                        static_cast<hipStream_t>(stream)),
+                 "backward kernels launch"))
+    return PLPSH_ERR_HIP;
+  return PLPSH_OK;
+}
+
 }  // extern "C"
+

@@ -88,6 +88,7 @@ struct HeadScale { float beta[256]; };   // log2(e) / sigma_h (dense ALiBi)
 struct FwdArgs {
   const void* q; const void* k; const void* v; void* o;
   const PlanRec* plan;
+  float* lse;  // optional: log of each row's normaliser, [B, Hq, n]
   int B, Hq, Hkv, n, s, ntile, cs;
 };
 
@@ -986,6 +987,11 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
     const float l = xsum16(f.lsum[rb]);
     const float inv = 1.0f / l;
     if (f.R[rb] >= n) continue;
+    if constexpr (MODE != MODE_ALIBI) {
+      // log sum_j c C e^S = ln 2 (Msc + log2 l): the weights were e^{S - Msc ln 2}
+      if (A.lse != nullptr && g == 0)
+        A.lse[static_cast<size_t>(b * A.Hq + h) * n + f.R[rb]] = 0.6931471805599453f * (f.Msc[rb] + log2f(l));
+    }
     T* orow = Op + static_cast<size_t>(f.R[rb]) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -1054,10 +1060,11 @@ int grid_size(int ntile, int instances, int* cs) {
 
 hipError_t launch_plsh_fwd(const void* q, const void* k, const void* v, void* o, int batch, int hq, int hkv,
                            int n, int d, int dtype, int s, int causal, const void* bins, const uint16_t* order,
-                           bool literal, hipStream_t st) {
+                           bool literal, float* lse, hipStream_t st) {
   const BinsLayout L = bins_layout(hq, s, n);
   FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o;
+  a.lse = lse;
   a.plan = reinterpret_cast<const PlanRec*>(static_cast<const char*>(bins) + L.off_plan);
   a.B = batch; a.Hq = hq; a.Hkv = hkv; a.n = n; a.s = s;
   a.ntile = (n + BM - 1) / BM;
@@ -1073,6 +1080,7 @@ hipError_t launch_alibi_fwd(const void* q, const void* k, const void* v, void* o
                             int n, int d, int dtype, const float* beta, int causal, hipStream_t st) {
   FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o;
+  a.lse = nullptr;
   a.plan = nullptr;
   a.B = batch; a.Hq = hq; a.Hkv = hkv; a.n = n; a.s = 1;
   a.ntile = (n + BM - 1) / BM;

@@ -1,0 +1,544 @@
+// Backward pass of Positional-LSH attention, for training with the
+// approximation in place of exact ALiBi (explainer of arXiv 2605.09472, Key
+// results, experimental validation: Qwen3 trained from scratch, Mistral
+// fine-tuned with it).
+//
+// With W = c o C o exp(S), S = Q K^T / sqrt(d), P = W / (W 1) and the row
+// log-normaliser LSE saved by the forward pass (P = c o C o exp(S - LSE)):
+//   dV = P^T dO,  dP = dO V^T,  D_r = <dO_r, O_r>,  dS = P o (dP - D),
+//   dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d).
+// The counts c do not depend on Q, K, V; they are recomputed from the same
+// bins as the forward pass.
+//
+// One kernel template serves both directions.  A workgroup owns 128
+// consecutive positions ("own": query rows for dQ, keys for dK/dV; 8 waves of
+// 16) and walks 64-position tiles of the other side ("other": keys for dQ,
+// query rows for dK/dV) over the window where c can be non-zero.  In both
+// directions the products are laid out [other x own]:
+//   T1 = Ya Xa^T (S),  T2 = Yb Xb^T (dP),  Acc1 += Ya^T dS,  Acc2 += Yb^T P
+// with (Xa, Xb, Ya, Yb) = (Q, dO, K, V) for dQ and (K, V, Q, dO) for dK/dV;
+// Acc1 is dQ^T or dK^T, Acc2 (dK/dV only) dV^T.  The counts in the same
+// layout: far tiles as a product of an own-side and an other-side 0/1 factor
+// over the hashes (a block shared across a tile edge must contain that
+// edge), the tiles overlapping the own positions hash by hash.  c is
+// symmetric, so both directions use the same formulas.  With GQA the dK/dV
+// workgroup sums over the query heads of its KV head.
+#include <climits>
+#include <type_traits>
+
+#include "internal.h"
+
+namespace plpsh {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+typedef __attribute__((address_space(3))) unsigned char lds_uchar_t;
+
+constexpr int BM = 128;      // own positions per workgroup
+constexpr int NW = 8;        // waves, 16 own positions each
+constexpr int NT = 64 * NW;
+constexpr int BN = 64;       // other positions per tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D>
+struct BG {
+  static constexpr int RB = 2 * D;              // bytes per row (bf16)
+  static constexpr int CPR = RB / 16;           // 16-byte chunks per row
+  static constexpr int RPI = 1024 / RB;         // rows per 1 KB load instruction
+  static constexpr int TILE = BN * RB;
+  static constexpr int NI = TILE / 1024 / NW;   // load instructions per wave per matrix
+  static_assert(TILE % (1024 * NW) == 0, "tile loads split evenly over the waves");
+  static constexpr int STAGE = 2 * TILE + 512;  // Ya, Yb, then (dK/dV) LSE and D of the tile's rows
+  static constexpr int KS = D / 32;
+  static constexpr int DB = D / 16;
+  __device__ static int sw(int row) { return CPR >= 16 ? 2 * (row & 7) : 2 * (row & 3); }
+};
+constexpr int SM_HASH = 0;  // per hash: a, e, a2, e2 of the own tile (16 bytes)
+
+struct BwdArgs {
+  const void* q; const void* k; const void* v; const void* dout;
+  const float* lse; const float* dd;   // [B, Hq, n]
+  void* dq; void* dk; void* dv;
+  const PlanRec* plan;
+  int B, Hq, Hkv, n, s, ntile, cs;
+};
+struct BwdOrder { uint32_t w[512]; };  // instances (heads or KV groups), most expensive first, 16-bit entries
+
+__device__ __forceinline__ int order_get(const BwdOrder& o, int i) {
+  return static_cast<int>((o.w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+}
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_uchar_t*)(p)));
+}
+__device__ __forceinline__ u32x4 lds128_at(uint32_t a) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(static_cast<uintptr_t>(a));
+}
+__device__ __forceinline__ u32x2 lds_tr16_at(uint32_t a) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(static_cast<uintptr_t>(a)));
+  return __builtin_bit_cast(u32x2, v);
+}
+__device__ __forceinline__ float lds_f32_at(uint32_t a) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) float*>(static_cast<uintptr_t>(a));
+}
+
+// block [st, en) of own position r0 + p for one hash, from its plan record
+// fields (uniform): boundary bits, a (block of r0) and e2 (block of the
+// tile's last row)
+__device__ __forceinline__ void own_block(uint64_t lo64, uint64_t hi64, int a, int e2, int r0, int p, int& st,
+                                          int& en) {
+  const int q = p & 63;
+  const uint64_t le = q == 63 ? ~0ull : ((2ull << q) - 1);
+  const uint64_t half = p < 64 ? lo64 : hi64;
+  const uint64_t m = half & le, gt = half & ~le;
+  const int sp = m ? (p & 64) + 63 - __builtin_clzll(m) : ((p >= 64 && lo64) ? 63 - __builtin_clzll(lo64) : 0);
+  const int ep = gt ? (p & 64) + __builtin_ctzll(gt) : ((p < 64 && hi64) ? 64 + __builtin_ctzll(hi64) : BM);
+  st = sp ? r0 + sp : a;
+  en = ep < BM ? r0 + ep : e2;
+}
+
+template <int D, bool CAUSAL, int NCH, bool KEYSIDE>
+__global__ __launch_bounds__(NT, 1) void bwd_kernel(BwdArgs A, BwdOrder ord) {
+  using G = BG<D>;
+  using T = uint16_t;
+  constexpr int KS = G::KS, DB = G::DB;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  auto stage = [&](int i) { return smem + i * G::STAGE; };
+  unsigned char* sm = smem + 2 * G::STAGE;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = A.n, s = A.s;
+  const int grp = A.Hq / A.Hkv;
+
+  // ---- work item: consecutive own tiles of an instance stay on one XCD
+  const int gid = blockIdx.x;
+  const int xcd = gid & 7, kk = gid >> 3;
+  const int inst = kk / A.cs;
+  const int ot = xcd * A.cs + kk % A.cs;
+  if (ot >= A.ntile) return;
+  const int b = inst % A.B;
+  const int hsel = order_get(ord, inst / A.B);   // query head (dQ) or KV head (dK/dV)
+  const int o0 = ot * BM;
+  const int own = o0 + 16 * w + l16;             // this lane's own position
+  const int ownc = min(own, n - 1);
+
+  // ---- own-side operands (B of T1 and T2): 16 rows of Xa and Xb per wave
+  const T* Xa;
+  const T* Xb;
+  if constexpr (KEYSIDE) {
+    Xa = static_cast<const T*>(A.k) + static_cast<size_t>(b * A.Hkv + hsel) * n * D;
+    Xb = static_cast<const T*>(A.v) + static_cast<size_t>(b * A.Hkv + hsel) * n * D;
+  } else {
+    Xa = static_cast<const T*>(A.q) + static_cast<size_t>(b * A.Hq + hsel) * n * D;
+    Xb = static_cast<const T*>(A.dout) + static_cast<size_t>(b * A.Hq + hsel) * n * D;
+  }
+  u32x4 xa[KS], xb[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    xa[ks] = *reinterpret_cast<const u32x4*>(Xa + static_cast<size_t>(ownc) * D + 32 * ks + 8 * g);
+    xb[ks] = *reinterpret_cast<const u32x4*>(Xb + static_cast<size_t>(ownc) * D + 32 * ks + 8 * g);
+  }
+
+  // per-lane LDS offsets: tile loads, row-wise reads (T1, T2), transposed reads (Acc)
+  int loff[G::NI];
+#pragma unroll
+  for (int i = 0; i < G::NI; ++i) {
+    const int I = w * G::NI + i;
+    const int row = I * G::RPI + lane / G::CPR;
+    const int pc = lane % G::CPR;
+    loff[i] = row * G::RB + 16 * (pc ^ G::sw(row));  // global byte offset landing at LDS slot (row, pc)
+  }
+  const uint32_t rbase = l16 * G::RB + 16 * (g ^ G::sw(l16));  // row l16, chunk g; k-step ks: ^ 64 ks
+  int trbase;  // transposed read: rows 4g + (l16 >> 2) (+16), 8 bytes of column pair (l16 & 3)
+  {
+    const int a = l16 & 3, t = l16 >> 2;
+    const int key = 4 * g + t;
+    trbase = key * G::RB + 16 * ((a >> 1) ^ G::sw(key)) + 8 * (a & 1);
+  }
+
+  f32x4 acc1[DB], acc2[KEYSIDE ? DB : 1];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc1[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int db = 0; db < (KEYSIDE ? DB : 1); ++db) acc2[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float sc = rsqrtf(static_cast<float>(D)) * kLog2e;
+
+  // dK/dV: every query head of the KV group; dQ: the one head
+  const int nh = KEYSIDE ? grp : 1;
+  for (int hh = 0; hh < nh; ++hh) {
+    const int h = KEYSIDE ? hsel * grp + hh : hsel;  // query head (hashes, Q, dO, LSE, D)
+    const int kvh = KEYSIDE ? hsel : hsel / grp;
+    const T *Ya, *Yb;
+    if constexpr (KEYSIDE) {
+      Ya = static_cast<const T*>(A.q) + static_cast<size_t>(b * A.Hq + h) * n * D;
+      Yb = static_cast<const T*>(A.dout) + static_cast<size_t>(b * A.Hq + h) * n * D;
+    } else {
+      Ya = static_cast<const T*>(A.k) + static_cast<size_t>(b * A.Hkv + kvh) * n * D;
+      Yb = static_cast<const T*>(A.v) + static_cast<size_t>(b * A.Hkv + kvh) * n * D;
+    }
+    const float* lse_h = A.lse + static_cast<size_t>(b * A.Hq + h) * n;
+    const float* dd_h = A.dd + static_cast<size_t>(b * A.Hq + h) * n;
+
+    // plan records of the own tile: lane i holds hash i (and i + 64)
+    const PlanRec* rec = A.plan + (static_cast<size_t>(h) * A.ntile + ot) * s;
+    u32x4 pb[2], pr[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int i = lane + 64 * x;
+      const bool ok = (x == 0 || NCH == 4) && i < s;
+      const PlanRec* ri = rec + (i < s ? i : 0);
+      pb[x] = ok ? *reinterpret_cast<const u32x4*>(ri->bits) : u32x4{0, 0, 0, 0};
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ri);
+      // absent hashes never count: a = +inf, e = -inf, a2 = +inf, e2 = -inf
+      pr[x] = ok ? v : u32x4{0x7FFFFFFFu, 0x80000000u, 0x7FFFFFFFu, 0x80000000u};
+    }
+    // (a, e, a2, e2) of every hash slot into LDS for the count factors
+    __syncthreads();  // previous head's readers are done
+    if (w == 0) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int i = lane + 64 * x;
+        if (i < 32 * NCH) *reinterpret_cast<u32x4*>(sm + SM_HASH + 16 * i) = pr[x];
+      }
+    }
+    // window of other positions with weight: [lo, hi)
+    int vlo = static_cast<int>(pr[0][0]), vhi = static_cast<int>(pr[0][3]);
+    if constexpr (NCH == 4) {
+      vlo = min(vlo, static_cast<int>(pr[1][0]));
+      vhi = max(vhi, static_cast<int>(pr[1][3]));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      vlo = min(vlo, __shfl_xor(vlo, o, 64));
+      vhi = max(vhi, __shfl_xor(vhi, o, 64));
+    }
+    const int lo = __builtin_amdgcn_readfirstlane(vlo);
+    const int hi = __builtin_amdgcn_readfirstlane(vhi);
+    __syncthreads();
+
+    // own-side count factors over hash slots 32 ch + 8 g .. + 7:
+    // left of the own tile [own < e], right of it [own >= a2]
+    u32x4 fl[NCH], fr[NCH];
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      const unsigned char* hp = sm + SM_HASH + 16 * (32 * ch + 8 * g);
+#pragma unroll
+      for (int u2 = 0; u2 < 4; ++u2) {
+        const u32x4 r0v = *reinterpret_cast<const u32x4*>(hp + 16 * (2 * u2));
+        const u32x4 r1v = *reinterpret_cast<const u32x4*>(hp + 16 * (2 * u2 + 1));
+        fl[ch][u2] = (own < static_cast<int>(r0v[1]) ? 0x3F80u : 0u) |
+                     (own < static_cast<int>(r1v[1]) ? 0x3F800000u : 0u);
+        fr[ch][u2] = (own >= static_cast<int>(r0v[2]) ? 0x3F80u : 0u) |
+                     (own >= static_cast<int>(r1v[2]) ? 0x3F800000u : 0u);
+      }
+    }
+    // dQ: the own row's LSE (log2 units) and D
+    float lse2_own = 0.f, dd_own = 0.f;
+    if constexpr (!KEYSIDE) {
+      lse2_own = lse_h[ownc] * kLog2e;
+      dd_own = dd_h[ownc];
+    }
+
+    // ---- tile schedule: near tiles (overlapping the own positions), then
+    // left (other < own tile) and right (other >= own tile end), as the
+    // causal direction allows (dQ: other <= own; dK/dV: other >= own)
+    const int nown = min(BM, n - o0);
+    const int nnear = nown > BN ? 2 : 1;
+    const bool do_left = !CAUSAL || !KEYSIDE;
+    const bool do_right = !CAUSAL || KEYSIDE;
+    const int nleft = (do_left && lo < o0) ? (o0 - lo + BN - 1) / BN : 0;
+    const int nright = (do_right && hi > o0 + BM) ? (hi - (o0 + BM) + BN - 1) / BN : 0;
+    const int ntl = nnear + nleft + nright;
+    auto tile_j0 = [&](int t) {
+      return t < nnear ? o0 + BN * t
+                       : (t < nnear + nleft ? o0 - BN * (t - nnear + 1) : o0 + BM + BN * (t - nnear - nleft));
+    };
+    auto issue = [&](int t, unsigned char* st) {
+      const int j0 = tile_j0(t);
+      const int rows = n - j0;
+      const int nrec = rows > 0 ? rows * G::RB : 0;
+      const size_t off = static_cast<size_t>(j0) * G::RB;
+      const uint64_t ab = reinterpret_cast<uint64_t>(Ya) + off;
+      const uint64_t bb = reinterpret_cast<uint64_t>(Yb) + off;
+      const i32x4 ra = {static_cast<int>(ab), static_cast<int>((ab >> 32) & 0xFFFF), nrec, 0x00020000};
+      const i32x4 rb = {static_cast<int>(bb), static_cast<int>((bb >> 32) & 0xFFFF), nrec, 0x00020000};
+      const uint32_t l0 = lds_addr(st);
+#pragma unroll
+      for (int i = 0; i < G::NI; ++i) {
+        const int I = w * G::NI + i;
+        asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :
+                     : "v"(loff[i]), "s"(ra), "{m0}"(l0 + I * 1024)
+                     : "memory");
+        asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :
+                     : "v"(loff[i]), "s"(rb), "{m0}"(l0 + G::TILE + I * 1024)
+                     : "memory");
+      }
+      if constexpr (KEYSIDE) {
+        if (w == 0) {  // LSE and D of the tile's 64 rows
+          const int frec = rows > 0 ? min(rows, BN) * 4 : 0;
+          const uint64_t lb = reinterpret_cast<uint64_t>(lse_h + j0);
+          const uint64_t db2 = reinterpret_cast<uint64_t>(dd_h + j0);
+          const i32x4 rl = {static_cast<int>(lb), static_cast<int>((lb >> 32) & 0xFFFF), frec, 0x00020000};
+          const i32x4 rd = {static_cast<int>(db2), static_cast<int>((db2 >> 32) & 0xFFFF), frec, 0x00020000};
+          asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                       :
+                       : "v"(4 * lane), "s"(rl), "{m0}"(l0 + 2 * G::TILE)
+                       : "memory");
+          asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                       :
+                       : "v"(4 * lane), "s"(rd), "{m0}"(l0 + 2 * G::TILE + 256)
+                       : "memory");
+        }
+      }
+    };
+
+    // the own position's block of hash i (near counts), causal cut applied
+    auto own_interval = [&](int i, int& st, int& en) {
+      const uint32_t b0 = __builtin_amdgcn_readlane(i < 64 ? pb[0][0] : pb[1][0], i & 63);
+      const uint32_t b1 = __builtin_amdgcn_readlane(i < 64 ? pb[0][1] : pb[1][1], i & 63);
+      const uint32_t b2 = __builtin_amdgcn_readlane(i < 64 ? pb[0][2] : pb[1][2], i & 63);
+      const uint32_t b3 = __builtin_amdgcn_readlane(i < 64 ? pb[0][3] : pb[1][3], i & 63);
+      const int ai = __builtin_amdgcn_readlane(static_cast<int>(i < 64 ? pr[0][0] : pr[1][0]), i & 63);
+      const int ei = __builtin_amdgcn_readlane(static_cast<int>(i < 64 ? pr[0][3] : pr[1][3]), i & 63);
+      own_block(b0 | (static_cast<uint64_t>(b1) << 32), b2 | (static_cast<uint64_t>(b3) << 32), ai, ei, o0,
+                own - o0, st, en);
+      if constexpr (CAUSAL) {
+        if constexpr (KEYSIDE) st = max(st, own);      // rows r >= key
+        else en = min(en, own + 1);                     // keys j <= row
+      }
+    };
+
+    issue(0, stage(0));
+    for (int t = 0; t < ntl; ++t) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (t + 1 < ntl) issue(t + 1, stage((t + 1) & 1));
+      const unsigned char* st = stage(t & 1);
+      const int j0 = tile_j0(t);
+      const int kind = t < nnear ? 0 : (t < nnear + nleft ? 1 : 2);
+      const uint32_t ya = lds_addr(st), yb = lds_addr(st + G::TILE);
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const int jc = j0 + 32 * kc;
+        if (jc >= n) break;
+        // T1 = Ya Xa^T and T2 = Yb Xb^T for other positions jc + 16 kb2 + (row l16 of A)
+        f32x4 t1[2], t2[2], cc[2];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          t1[kb2] = f32x4{0.f, 0.f, 0.f, 0.f};
+          t2[kb2] = f32x4{0.f, 0.f, 0.f, 0.f};
+          cc[kb2] = f32x4{0.f, 0.f, 0.f, 0.f};
+          const uint32_t roff = (16 * (2 * kc + kb2)) * G::RB + rbase;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            t1[kb2] = mfma_bf16(lds128_at(ya + (roff ^ (64 * ks))), xa[ks], t1[kb2]);
+            t2[kb2] = mfma_bf16(lds128_at(yb + (roff ^ (64 * ks))), xb[ks], t2[kb2]);
+          }
+        }
+        // counts c[other, own] in the same layout
+        if (kind == 0) {
+          // near: hash by hash from the own position's blocks
+          for (int i = 0; i < s; ++i) {
+            int lo_i, hi_i;
+            own_interval(i, lo_i, hi_i);
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int j = jc + 16 * kb2 + 4 * g + e;
+                cc[kb2][e] += (j >= lo_i && j < hi_i) ? 1.0f : 0.0f;
+              }
+          }
+        } else {
+          // far: c = sum over hashes of [other factor] [own factor]; the
+          // other factor of row l16 of the A operand over slots 8 g .. + 7
+#pragma unroll
+          for (int kb2 = 0; kb2 < 2; ++kb2) {
+            const int jo = jc + 16 * kb2 + l16;
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch) {
+              const unsigned char* hp = sm + SM_HASH + 16 * (32 * ch + 8 * g);
+              u32x4 af;
+#pragma unroll
+              for (int u2 = 0; u2 < 4; ++u2) {
+                const u32x4 r0v = *reinterpret_cast<const u32x4*>(hp + 16 * (2 * u2));
+                const u32x4 r1v = *reinterpret_cast<const u32x4*>(hp + 16 * (2 * u2 + 1));
+                if (kind == 1)  // left: [other >= a]
+                  af[u2] = (jo >= static_cast<int>(r0v[0]) ? 0x3F80u : 0u) |
+                           (jo >= static_cast<int>(r1v[0]) ? 0x3F800000u : 0u);
+                else  // right: [other < e2]
+                  af[u2] = (jo < static_cast<int>(r0v[3]) ? 0x3F80u : 0u) |
+                           (jo < static_cast<int>(r1v[3]) ? 0x3F800000u : 0u);
+              }
+              cc[kb2] = mfma_bf16(af, kind == 1 ? fl[ch] : fr[ch], cc[kb2]);
+            }
+          }
+        }
+        // P and dS; the row of each element is own (dQ) or other (dK/dV)
+        float p[2][4], ds[2][4];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float l2, dr;
+            if constexpr (KEYSIDE) {
+              const int rr = 16 * (2 * kc + kb2) + 4 * g + e;  // row within the tile
+              l2 = lds_f32_at(ya + 2 * G::TILE + 4 * rr) * kLog2e;
+              dr = lds_f32_at(ya + 2 * G::TILE + 256 + 4 * rr);
+            } else {
+              l2 = lse2_own;
+              dr = dd_own;
+            }
+            // for counted pairs the exponent is <= 0 (c e^(S - LSE) <= 1); the
+            // clamp keeps uncounted ones finite so that c = 0 zeroes them
+            const float x = fminf(fmaf(t1[kb2][e], sc, -l2), 0.0f);
+            const float pv = cc[kb2][e] * __builtin_amdgcn_exp2f(x);
+            p[kb2][e] = pv;
+            ds[kb2][e] = pv * (t2[kb2][e] - dr);
+          }
+        const u32x4 sf = {pack_bf16(ds[0][0], ds[0][1]), pack_bf16(ds[0][2], ds[0][3]),
+                          pack_bf16(ds[1][0], ds[1][1]), pack_bf16(ds[1][2], ds[1][3])};
+        const u32x4 pf = {pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]), pack_bf16(p[1][0], p[1][1]),
+                          pack_bf16(p[1][2], p[1][3])};
+        // Acc1 += Ya^T dS, Acc2 += Yb^T P (transposed reads of the staged tiles)
+        const uint32_t tro = (32 * kc) * G::RB + trbase;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const uint32_t a0 = (ya + tro) ^ (32 * db);
+          const u32x2 v0 = lds_tr16_at(a0);
+          const u32x2 v1 = lds_tr16_at(a0 + 16 * G::RB);
+          acc1[db] = mfma_bf16(u32x4{v0[0], v0[1], v1[0], v1[1]}, sf, acc1[db]);
+          if constexpr (KEYSIDE) {
+            const uint32_t b0 = (yb + tro) ^ (32 * db);
+            const u32x2 w0 = lds_tr16_at(b0);
+            const u32x2 w1 = lds_tr16_at(b0 + 16 * G::RB);
+            acc2[db] = mfma_bf16(u32x4{w0[0], w0[1], w1[0], w1[1]}, pf, acc2[db]);
+          }
+        }
+        (void)pf;
+      }
+    }
+  }
+
+  // ---- epilogue: Acc1 is dQ^T or dK^T (times sqrt(d) too much), Acc2 dV^T
+  if (own >= n) return;
+  const float rs = rsqrtf(static_cast<float>(D));
+  T* o1;
+  if constexpr (KEYSIDE) o1 = static_cast<T*>(A.dk) + (static_cast<size_t>(b * A.Hkv + hsel) * n + own) * D;
+  else o1 = static_cast<T*>(A.dq) + (static_cast<size_t>(b * A.Hq + hsel) * n + own) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const f32x4 x = acc1[db] * rs;
+    *reinterpret_cast<u32x2*>(o1 + 16 * db + 4 * g) = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+  }
+  if constexpr (KEYSIDE) {
+    T* o2 = static_cast<T*>(A.dv) + (static_cast<size_t>(b * A.Hkv + hsel) * n + own) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const f32x4 x = acc2[db];
+      *reinterpret_cast<u32x2*>(o2 + 16 * db + 4 * g) = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+    }
+  }
+}
+
+// D_r = <dO_r, O_r> for every (batch, query head, row): one wave per row
+template <int D>
+__global__ __launch_bounds__(256) void rowdot_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
+                                                     size_t rows, float* __restrict__ dd) {
+  const size_t r = static_cast<size_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  float acc = 0.f;
+  for (int c = lane; c < D; c += 64) {
+    const float a = __uint_as_float(static_cast<uint32_t>(o[r * D + c]) << 16);
+    const float b = __uint_as_float(static_cast<uint32_t>(dout[r * D + c]) << 16);
+    acc = fmaf(a, b, acc);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (lane == 0) dd[r] = acc;
+}
+
+template <int D, bool CAUSAL, int NCH, bool KEYSIDE>
+hipError_t launch_bwd_one(const BwdArgs& a, const BwdOrder& ord, int grid, hipStream_t st) {
+  constexpr int lds = 2 * BG<D>::STAGE + 16 * 128;
+  auto kfn = bwd_kernel<D, CAUSAL, NCH, KEYSIDE>;
+  static bool attr = false;  // benign race: idempotent
+  if (lds > 64 * 1024 && !attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL(kfn, dim3(grid), dim3(NT), lds, st, a, ord);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool KEYSIDE>
+hipError_t launch_bwd_nch(const BwdArgs& a, const BwdOrder& o, int grid, hipStream_t st) {
+  if (a.s <= 32) return launch_bwd_one<D, CAUSAL, 1, KEYSIDE>(a, o, grid, st);
+  if (a.s <= 64) return launch_bwd_one<D, CAUSAL, 2, KEYSIDE>(a, o, grid, st);
+  return launch_bwd_one<D, CAUSAL, 4, KEYSIDE>(a, o, grid, st);
+}
+
+template <bool KEYSIDE>
+hipError_t launch_bwd_dir(const BwdArgs& a, const BwdOrder& o, int d, int causal, int grid, hipStream_t st) {
+  if (d == 64) return causal ? launch_bwd_nch<64, true, KEYSIDE>(a, o, grid, st)
+                             : launch_bwd_nch<64, false, KEYSIDE>(a, o, grid, st);
+  if (d == 128) return causal ? launch_bwd_nch<128, true, KEYSIDE>(a, o, grid, st)
+                              : launch_bwd_nch<128, false, KEYSIDE>(a, o, grid, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_plsh_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, void* dq, void* dk, void* dv, int batch, int hq, int hkv, int n, int d,
+                           int s, int causal, const void* bins, const uint16_t* head_order, const uint16_t* kv_order,
+                           float* dd, hipStream_t st) {
+  const size_t rows = static_cast<size_t>(batch) * hq * n;
+  if (d == 64) {
+    hipLaunchKernelGGL(rowdot_kernel<64>, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dout), rows, dd);
+  } else {
+    hipLaunchKernelGGL(rowdot_kernel<128>, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dout), rows, dd);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.dout = dout;
+  a.lse = lse; a.dd = dd;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.plan = reinterpret_cast<const PlanRec*>(static_cast<const char*>(bins) + bins_layout(hq, s, n).off_plan);
+  a.B = batch; a.Hq = hq; a.Hkv = hkv; a.n = n; a.s = s;
+  a.ntile = (n + BM - 1) / BM;
+  a.cs = (a.ntile + 7) / 8;
+  BwdOrder oq{}, okv{};
+  for (int i = 0; i < hq; ++i) oq.w[i >> 1] |= static_cast<uint32_t>(head_order[i]) << (16 * (i & 1));
+  for (int i = 0; i < hkv; ++i) okv.w[i >> 1] |= static_cast<uint32_t>(kv_order[i]) << (16 * (i & 1));
+  e = launch_bwd_dir<false>(a, oq, d, causal, 8 * a.cs * batch * hq, st);
+  if (e != hipSuccess) return e;
+  return launch_bwd_dir<true>(a, okv, d, causal, 8 * a.cs * batch * hkv, st);
+}
+
+}  // namespace plpsh

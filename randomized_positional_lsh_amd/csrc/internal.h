@@ -32,11 +32,17 @@ hipError_t launch_bins(const double* du, int heads, int s, int n, void* bins, hi
 hipError_t launch_plsh_fwd(const void* q, const void* k, const void* v, void* o,
                            int batch, int hq, int hkv, int n, int d, int dtype,
                            int s, int causal, const void* bins, const uint16_t* head_order,
-                           bool literal, hipStream_t st);
+                           bool literal, float* lse, hipStream_t st);
 
 hipError_t launch_alibi_fwd(const void* q, const void* k, const void* v, void* o,
                             int batch, int hq, int hkv, int n, int d, int dtype,
                             const float* beta_host, int causal, hipStream_t st);
+
+// Backward pass (bwd.hip), bf16: dd receives D_r = <dO_r, O_r>, batch*hq*n floats.
+hipError_t launch_plsh_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, void* dq, void* dk, void* dv, int batch, int hq, int hkv, int n, int d,
+                           int s, int causal, const void* bins, const uint16_t* head_order, const uint16_t* kv_order,
+                           float* dd, hipStream_t st);
 
 // Error of the mask mean against L* (errnorm.hip).  `plan` is the plan-record
 // array of one head; scratch for the products is err_scan_bytes(n) bytes.

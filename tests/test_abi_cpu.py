@@ -182,6 +182,32 @@ def test_error_functions_validation():
     assert call(args(wsb=100)) == B.WORKSPACE_TOO_SMALL
 
 
+def test_backward_validation():
+    lib = B.raw()
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, batch=1, hq=2, hkv=1,
+                n=64, d=64, dtype=1, s=4, causal=1, bins=FAKE, binsb=1 << 30, ws=FAKE, wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.plpsh_attention_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                                       a["batch"], a["hq"], a["hkv"], a["n"], a["d"], a["dtype"], a["s"],
+                                       a["causal"], a["bins"], a["binsb"], None, a["ws"], a["wsb"], None)
+    for kw in [dict(lse=None), dict(do=None), dict(dk=None), dict(dv=None), dict(o=None), dict(ws=None),
+               dict(ws=ctypes.c_void_p((1 << 20) + 16)), dict(do=ctypes.c_void_p((1 << 20) + 4)), dict(hkv=3),
+               dict(s=0), dict(causal=2), dict(bins=None)]:
+        assert call(**kw) == B.INVALID_ARGUMENT, kw
+    assert call(dtype=0) == B.UNSUPPORTED
+    assert call(d=80) == B.UNSUPPORTED
+    assert call(wsb=16) == B.WORKSPACE_TOO_SMALL
+    assert call(binsb=16) == B.WORKSPACE_TOO_SMALL
+    assert call(batch=0) == B.OK and call(n=0) == B.OK  # empty: nothing launched
+    assert lib.plpsh_attention_bwd_workspace_bytes(2, 4, 100) >= 2 * 4 * 100 * 4
+    assert lib.plpsh_attention_bwd_workspace_bytes(1, 0, 100) == 0
+    # forward with normalisers: lse is required
+    st = lib.plpsh_attention_fwd_lse(FAKE, FAKE, FAKE, FAKE, None, 1, 2, 1, 64, 64, 1, 4, 1, FAKE, 1 << 30, None, None)
+    assert st == B.INVALID_ARGUMENT
+
+
 def test_draw_validation():
     lib = B.raw()
     sig = np.array([1.0])
