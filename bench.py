@@ -364,6 +364,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-crossover", action="store_true")
     ap.add_argument("--no-convergence", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-literal", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true", help="only run a 1 GiB device copy (counter scaling)")
     args = ap.parse_args()
 
@@ -425,13 +427,14 @@ def main():
                    "sigma": "2^(8(h+1)/H)", "parallelism": "single GPU"},
         "roofline": roofline,
     }
-    if W.dtype == "bf16":
+    if W.dtype == "bf16" and not args.no_backward:
         line["backward"] = backward(P, W, run, flops)
         log(f"backward {line['backward']}")
-    lms = literal(run)
-    line["literal"] = {"kernel_ms": round(lms, 4), "fused_kernel_ms": round(kern_ms, 4),
-                       "slowdown_vs_fused": round(lms / kern_ms, 2)}
-    log(f"literal per-hash attention kernel {lms:.4f} ms")
+    if not args.no_literal:
+        lms = literal(run)
+        line["literal"] = {"kernel_ms": round(lms, 4), "fused_kernel_ms": round(kern_ms, 4),
+                           "slowdown_vs_fused": round(lms / kern_ms, 2)}
+        log(f"literal per-hash attention kernel {lms:.4f} ms")
     if not args.no_dense:
         dms = dense_alibi(P, W, q, k, v)
         line["dense_alibi"] = {"ms": round(dms, 4), "tokens_per_s": round(tokens / (dms * 1e-3), 1),

@@ -2,11 +2,13 @@
 
   python -m randomized_positional_lsh_amd.profsum stats DIR OUT.md --cmd "..."
       Per-kernel rows (calls, mean / min / max duration) of the
-      --kernel-trace --stats CSV in DIR for the kernels of this library.
+      --kernel-trace --stats CSV in DIR for the kernels of this library,
+      labelled by kernel and template instance.
 
   python -m randomized_positional_lsh_amd.profsum traffic FETCH WRITE CFETCH CWRITE OUT.json \
           --workload mistral --kernel-sha SHA --copy-bytes N --cmd "..."
-      HBM bytes per launch of the attention kernel from two --pmc runs
+      HBM bytes per launch of the count-weighted attention kernel at the
+      Mistral shape (fwd_kernel<128, bf16, causal, 1 hash chunk, mode 0>) from two --pmc runs
       (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), each scaled by the factor
       that makes the same counter read right on plain device copies of
       known total size (CFETCH / CWRITE runs, N bytes read and N written).
@@ -19,9 +21,27 @@ import csv
 import glob
 import json
 import os
+import re
 import statistics
 
-KERNELS = {"fwd_kernel": "attention (fwd_kernel)", "bins_kernel": "bin boundaries (bins_kernel)"}
+# Kernel labels.  rocprofv3 reports demangled names; the attention template's
+# arguments are <head_dim, bf16, causal, hash chunks, mode> with mode 0
+# count-weighted, 1 dense ALiBi, 2 one short attention per hash; the backward
+# template's <head_dim, causal, hash chunks, keys side>.
+MAIN = "fwd_kernel<128, true, true, 1, 0>"
+_MODES = {"0": "attention, count-weighted", "1": "dense exact ALiBi", "2": "one attention per hash"}
+_PLAIN = [
+    ("bins_kernel", "bin boundaries"),
+    ("rowdot_kernel", "backward D = <dO, O>"),
+    ("rowmax_kernel", "error row maxima"),
+    ("scan_local_kernel", "error product, tile scans"),
+    ("scan_carry_kernel", "error product, carries"),
+    ("combine_kernel", "error product, combine"),
+    ("dots_kernel", "Lanczos dot products"),
+    ("sub_proj_kernel", "Lanczos projections"),
+    ("scale_kernel", "Lanczos scaling"),
+    ("argmax_kernel", "max reduction"),
+]
 
 
 def _one(pattern: str) -> str:
@@ -32,9 +52,16 @@ def _one(pattern: str) -> str:
 
 
 def _short(name: str) -> str | None:
-    for k, v in KERNELS.items():
+    m = re.search(r"fwd_kernel<(\d+), (\w+), (\w+), (\d+), (\d)>", name)
+    if m:
+        return f"{_MODES[m.group(5)]} (fwd_kernel<{', '.join(m.groups())}>)"
+    m = re.search(r"bwd_kernel<(\d+), (\w+), (\d+), (\w+)>", name)
+    if m:
+        side = "dK dV" if m.group(4) == "true" else "dQ"
+        return f"backward {side} (bwd_kernel<{', '.join(m.groups())}>)"
+    for k, v in _PLAIN:
         if k in name:
-            return v
+            return f"{v} ({k})"
     return None
 
 
@@ -69,8 +96,8 @@ def _counter_kib(d: str, regex_part: str, counter: str) -> list[float]:
 
 def traffic(fetch: str, write: str, cfetch: str, cwrite: str, out: str, workload: str, sha: str,
             copy_bytes: int, cmd: str) -> None:
-    f = _counter_kib(fetch, "fwd_kernel", "FETCH_SIZE")
-    w = _counter_kib(write, "fwd_kernel", "WRITE_SIZE")
+    f = _counter_kib(fetch, MAIN, "FETCH_SIZE")
+    w = _counter_kib(write, MAIN, "WRITE_SIZE")
     cf = sum(_counter_kib(cfetch, "copyBuffer", "FETCH_SIZE")) * 1024.0
     cw = sum(_counter_kib(cwrite, "copyBuffer", "WRITE_SIZE")) * 1024.0
     sf, sw = copy_bytes / cf, copy_bytes / cw
