@@ -59,9 +59,19 @@ struct BG {
   static constexpr int STAGE = 2 * TILE + 512;  // Ya, Yb, then (dK/dV) LSE and D of the tile's rows
   static constexpr int KS = D / 32;
   static constexpr int DB = D / 16;
+  // near-count matrix H[p][own] (biased int16, p <= 128): in stage 1 while
+  // the counts are set up when it fits, else a region of its own
+  static constexpr int HC = (BM + 1) * BM * 2;
+  static constexpr int HOFF = HC <= STAGE ? STAGE : 2 * STAGE;
+  static constexpr int BIG = HC <= STAGE ? 2 * STAGE : 2 * STAGE + HC;
   __device__ static int sw(int row) { return CPR >= 16 ? 2 * (row & 7) : 2 * (row & 3); }
 };
-constexpr int SM_HASH = 0;  // per hash: a, e, a2, e2 of the own tile (16 bytes)
+// small-LDS region
+constexpr int SM_HASH = 0;                   // per hash slot: a, e, a2, e2 of the own tile (16 bytes)
+constexpr int SM_TH = SM_HASH + 128 * 16;    // 9 x 16-byte bf16 prefixes of ones
+constexpr int SM_LO = SM_TH + 256;           // per own position: support [lo, hi)
+constexpr int SM_HI = SM_LO + 4 * BM;
+constexpr int SMALL = SM_HI + 4 * BM;
 
 struct BwdArgs {
   const void* q; const void* k; const void* v; const void* dout;
@@ -96,6 +106,31 @@ __device__ __forceinline__ u32x2 lds_tr16_at(uint32_t a) {
 __device__ __forceinline__ float lds_f32_at(uint32_t a) {
   return *reinterpret_cast<const __attribute__((address_space(3))) float*>(static_cast<uintptr_t>(a));
 }
+__device__ __forceinline__ u32x2 lds_tr16(const unsigned char* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(const_cast<unsigned char*>(p)));
+  return __builtin_bit_cast(u32x2, v);
+}
+__device__ __forceinline__ u32x4 lds128(const unsigned char* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+__device__ __forceinline__ int clamp08(int x) { return min(max(x, 0), 8); }
+// near counts: 16-bit integers biased by 2^15, two per dword, integer LDS atomics
+constexpr uint32_t kBias2 = 0x80008000u;
+__device__ __forceinline__ void lds_add(unsigned char* p, uint32_t v) {
+  __hip_atomic_fetch_add(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_sub(unsigned char* p, uint32_t v) {
+  __hip_atomic_fetch_sub(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// two biased 16-bit counts -> two bf16 (exact for |count| <= 256)
+__device__ __forceinline__ uint32_t biased_to_bf16x2(uint32_t x) {
+  const float lo = __uint_as_float(0x4B000000u | (x & 0xFFFFu)) - 8421376.0f;
+  const float hi = __uint_as_float(0x4B000000u | (x >> 16)) - 8421376.0f;
+  return pack_bf16(lo, hi);
+}
 
 // block [st, en) of own position r0 + p for one hash, from its plan record
 // fields (uniform): boundary bits, a (block of r0) and e2 (block of the
@@ -119,7 +154,8 @@ __global__ __launch_bounds__(NT, 1) void bwd_kernel(BwdArgs A, BwdOrder ord) {
   constexpr int KS = G::KS, DB = G::DB;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   auto stage = [&](int i) { return smem + i * G::STAGE; };
-  unsigned char* sm = smem + 2 * G::STAGE;
+  unsigned char* hc = smem + G::HOFF;
+  unsigned char* sm = smem + G::BIG;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
@@ -209,7 +245,8 @@ __global__ __launch_bounds__(NT, 1) void bwd_kernel(BwdArgs A, BwdOrder ord) {
       // absent hashes never count: a = +inf, e = -inf, a2 = +inf, e2 = -inf
       pr[x] = ok ? v : u32x4{0x7FFFFFFFu, 0x80000000u, 0x7FFFFFFFu, 0x80000000u};
     }
-    // (a, e, a2, e2) of every hash slot into LDS for the count factors
+    // (a, e, a2, e2) of every hash slot into LDS for the far-count factors;
+    // the near-count matrix cleared; supports reset
     __syncthreads();  // previous head's readers are done
     if (w == 0) {
 #pragma unroll
@@ -217,6 +254,17 @@ __global__ __launch_bounds__(NT, 1) void bwd_kernel(BwdArgs A, BwdOrder ord) {
         const int i = lane + 64 * x;
         if (i < 32 * NCH) *reinterpret_cast<u32x4*>(sm + SM_HASH + 16 * i) = pr[x];
       }
+    }
+    for (int x = tid; x < G::HC / 16; x += NT) reinterpret_cast<u32x4*>(hc)[x] = u32x4{kBias2, kBias2, kBias2, kBias2};
+    if (tid < 9) {
+      u32x4 pth;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) pth[qq] = (tid >= 2 * qq + 2) ? 0x3F803F80u : (tid == 2 * qq + 1 ? 0x00003F80u : 0u);
+      *reinterpret_cast<u32x4*>(sm + SM_TH + 16 * tid) = pth;
+    }
+    if (tid < BM) {
+      reinterpret_cast<int*>(sm + SM_LO)[tid] = INT_MAX;
+      reinterpret_cast<int*>(sm + SM_HI)[tid] = INT_MIN;
     }
     // window of other positions with weight: [lo, hi)
     int vlo = static_cast<int>(pr[0][0]), vhi = static_cast<int>(pr[0][3]);
@@ -231,7 +279,110 @@ __global__ __launch_bounds__(NT, 1) void bwd_kernel(BwdArgs A, BwdOrder ord) {
     }
     const int lo = __builtin_amdgcn_readfirstlane(vlo);
     const int hi = __builtin_amdgcn_readfirstlane(vhi);
-    __syncthreads();
+    lds_barrier();
+    {
+      // H[own][p] (stored [p][own]) by atomic adds: wave w takes the hashes
+      // i = w mod NW for all 128 own positions (lane and 64 + lane): +1 at
+      // the start of the position's block (0 when it starts before the
+      // tile), -1 at its end (the spare row 128 when past the tile).  The
+      // same pass gives each own position its support: the least block
+      // start and the greatest block end over the hashes.
+      const uint64_t le = lane == 63 ? ~0ull : ((2ull << lane) - 1);
+      unsigned char* col0 = hc + 2 * (lane - (lane & 1));
+      unsigned char* col1 = col0 + 2 * 64;
+      const uint32_t onev = 1u << (16 * (lane & 1));
+      int lo0 = INT_MAX, hi0 = INT_MIN, lo1 = INT_MAX, hi1 = INT_MIN;
+      int nfull = 0, flo = INT_MAX, fhi = INT_MIN;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        if (x == 1 && NCH != 4) break;
+        const int iend = min(s, 64 * x + 64);
+        for (int i = 64 * x + w; i < iend; i += NW) {
+          const uint32_t b0 = __builtin_amdgcn_readlane(pb[x][0], i & 63);
+          const uint32_t b1 = __builtin_amdgcn_readlane(pb[x][1], i & 63);
+          const uint32_t b2 = __builtin_amdgcn_readlane(pb[x][2], i & 63);
+          const uint32_t b3 = __builtin_amdgcn_readlane(pb[x][3], i & 63);
+          const int ai = __builtin_amdgcn_readlane(static_cast<int>(pr[x][0]), i & 63);
+          const int ei = __builtin_amdgcn_readlane(static_cast<int>(pr[x][3]), i & 63);
+          const uint64_t lo64 = b0 | (static_cast<uint64_t>(b1) << 32);
+          const uint64_t hi64 = b2 | (static_cast<uint64_t>(b3) << 32);
+          if ((lo64 | hi64) == 0) {  // one block over the whole tile
+            ++nfull;
+            flo = min(flo, ai);
+            fhi = max(fhi, ei);
+            continue;
+          }
+          const uint64_t m0 = lo64 & le, g0 = lo64 & ~le;
+          const int st0 = m0 ? 63 - __builtin_clzll(m0) : 0;
+          const int en0 = g0 ? __builtin_ctzll(g0) : (hi64 ? 64 + __builtin_ctzll(hi64) : BM);
+          const uint64_t m1 = hi64 & le, g1 = hi64 & ~le;
+          const int st1 = m1 ? 127 - __builtin_clzll(m1) : (lo64 ? 63 - __builtin_clzll(lo64) : 0);
+          const int en1 = g1 ? 64 + __builtin_ctzll(g1) : BM;
+          lds_add(col0 + st0 * (2 * BM), onev);
+          lds_sub(col0 + en0 * (2 * BM), onev);
+          lds_add(col1 + st1 * (2 * BM), onev);
+          lds_sub(col1 + en1 * (2 * BM), onev);
+          lo0 = min(lo0, st0 ? o0 + st0 : ai);
+          hi0 = max(hi0, en0 < BM ? o0 + en0 : ei);
+          lo1 = min(lo1, st1 ? o0 + st1 : ai);
+          hi1 = max(hi1, en1 < BM ? o0 + en1 : ei);
+        }
+      }
+      if (nfull > 0) {
+        lds_add(col0, static_cast<uint32_t>(nfull) * onev);
+        lds_add(col1, static_cast<uint32_t>(nfull) * onev);
+      }
+      lo0 = min(lo0, flo);
+      lo1 = min(lo1, flo);
+      hi0 = max(hi0, fhi);
+      hi1 = max(hi1, fhi);
+      int* sLo = reinterpret_cast<int*>(sm + SM_LO);
+      int* sHi = reinterpret_cast<int*>(sm + SM_HI);
+      __hip_atomic_fetch_min(sLo + lane, lo0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_fetch_max(sHi + lane, hi0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_fetch_min(sLo + 64 + lane, lo1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_fetch_max(sHi + 64 + lane, hi1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    lds_barrier();
+    // H operand of this lane's own position through transposing reads of the
+    // [p][own] matrix, and the count before each 32-position chunk
+    u32x4 hf[4];
+    float nbase[4];
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      const int p0 = 32 * ch + 8 * g;
+      const unsigned char* base = hc + (p0 + (l16 >> 2)) * (2 * BM) + 2 * (16 * w + 4 * (l16 & 3));
+      const u32x2 x0 = lds_tr16(base);
+      const u32x2 x1 = lds_tr16(base + 4 * (2 * BM));
+      hf[ch] = u32x4{biased_to_bf16x2(x0[0]), biased_to_bf16x2(x0[1]), biased_to_bf16x2(x1[0]),
+                     biased_to_bf16x2(x1[1])};
+      int csum = -8 * 32768;
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq)
+        csum += static_cast<int>((x0[qq] & 0xFFFFu) + (x0[qq] >> 16) + (x1[qq] & 0xFFFFu) + (x1[qq] >> 16));
+      csum += __shfl_xor(csum, 16, 64);
+      csum += __shfl_xor(csum, 32, 64);
+      nbase[ch] = static_cast<float>(csum);
+    }
+    {
+      float run = 0.0f;
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) {
+        const float sum = nbase[ch];
+        nbase[ch] = run;
+        run += sum;
+      }
+    }
+    // support of the own position (causal cut included); wave-uniform
+    // bounds of the wave's first and last position
+    int lo_own = reinterpret_cast<const int*>(sm + SM_LO)[16 * w + l16];
+    int hi_own = reinterpret_cast<const int*>(sm + SM_HI)[16 * w + l16];
+    if constexpr (CAUSAL) {
+      if constexpr (KEYSIDE) lo_own = max(lo_own, own);
+      else hi_own = min(hi_own, own + 1);
+    }
+    const int loF = __builtin_amdgcn_readlane(lo_own, 0);
+    const int hiL = __builtin_amdgcn_readlane(hi_own, 15);
 
     // own-side count factors over hash slots 32 ch + 8 g .. + 7:
     // left of the own tile [own < e], right of it [own >= a2]
@@ -311,35 +462,22 @@ __global__ __launch_bounds__(NT, 1) void bwd_kernel(BwdArgs A, BwdOrder ord) {
       }
     };
 
-    // the own position's block of hash i (near counts), causal cut applied
-    auto own_interval = [&](int i, int& st, int& en) {
-      const uint32_t b0 = __builtin_amdgcn_readlane(i < 64 ? pb[0][0] : pb[1][0], i & 63);
-      const uint32_t b1 = __builtin_amdgcn_readlane(i < 64 ? pb[0][1] : pb[1][1], i & 63);
-      const uint32_t b2 = __builtin_amdgcn_readlane(i < 64 ? pb[0][2] : pb[1][2], i & 63);
-      const uint32_t b3 = __builtin_amdgcn_readlane(i < 64 ? pb[0][3] : pb[1][3], i & 63);
-      const int ai = __builtin_amdgcn_readlane(static_cast<int>(i < 64 ? pr[0][0] : pr[1][0]), i & 63);
-      const int ei = __builtin_amdgcn_readlane(static_cast<int>(i < 64 ? pr[0][3] : pr[1][3]), i & 63);
-      own_block(b0 | (static_cast<uint64_t>(b1) << 32), b2 | (static_cast<uint64_t>(b3) << 32), ai, ei, o0,
-                own - o0, st, en);
-      if constexpr (CAUSAL) {
-        if constexpr (KEYSIDE) st = max(st, own);      // rows r >= key
-        else en = min(en, own + 1);                     // keys j <= row
-      }
-    };
-
     issue(0, stage(0));
-    for (int t = 0; t < ntl; ++t) {
+    // one tile; the kind (near, left, right) is a compile-time constant so
+    // that each phase's count operands die with it
+    auto tile = [&](auto kind_c, int t) {
+      constexpr int kind = decltype(kind_c)::value;
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (t + 1 < ntl) issue(t + 1, stage((t + 1) & 1));
       const unsigned char* st = stage(t & 1);
       const int j0 = tile_j0(t);
-      const int kind = t < nnear ? 0 : (t < nnear + nleft ? 1 : 2);
       const uint32_t ya = lds_addr(st), yb = lds_addr(st + G::TILE);
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
         const int jc = j0 + 32 * kc;
-        if (jc >= n) break;
+        // chunks outside every own position's support of this wave
+        if (jc >= n || jc + 32 <= loF || jc >= hiL) continue;
         // T1 = Ya Xa^T and T2 = Yb Xb^T for other positions jc + 16 kb2 + (row l16 of A)
         f32x4 t1[2], t2[2], cc[2];
 #pragma unroll
@@ -355,18 +493,25 @@ __global__ __launch_bounds__(NT, 1) void bwd_kernel(BwdArgs A, BwdOrder ord) {
           }
         }
         // counts c[other, own] in the same layout
-        if (kind == 0) {
-          // near: hash by hash from the own position's blocks
-          for (int i = 0; i < s; ++i) {
-            int lo_i, hi_i;
-            own_interval(i, lo_i, hi_i);
+        if constexpr (kind == 0) {
+          // near: c = count before the position chunk + prefix of H within
+          // it (a product with a table of prefixes of ones), then the causal
+          // cut (dQ: other <= own; dK/dV: other >= own)
+          // near tile t covers positions o0 + 64 t ..: position chunk 2 t + kc
+          const u32x4 hsel = t == 0 ? hf[kc] : hf[2 + kc];
+          const float b0 = t == 0 ? nbase[kc] : nbase[2 + kc];
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
+          for (int kb2 = 0; kb2 < 2; ++kb2) {
+            const u32x4 th = lds128(sm + SM_TH + 16 * clamp08(16 * kb2 + l16 - 8 * g + 1));
+            cc[kb2] = mfma_bf16(th, hsel, f32x4{b0, b0, b0, b0});
+            if constexpr (CAUSAL) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int j = jc + 16 * kb2 + 4 * g + e;
-                cc[kb2][e] += (j >= lo_i && j < hi_i) ? 1.0f : 0.0f;
+                const bool ok = KEYSIDE ? j >= own : j <= own;
+                cc[kb2][e] = ok ? cc[kb2][e] : 0.0f;
               }
+            }
           }
         } else {
           // far: c = sum over hashes of [other factor] [own factor]; the
@@ -382,14 +527,15 @@ __global__ __launch_bounds__(NT, 1) void bwd_kernel(BwdArgs A, BwdOrder ord) {
               for (int u2 = 0; u2 < 4; ++u2) {
                 const u32x4 r0v = *reinterpret_cast<const u32x4*>(hp + 16 * (2 * u2));
                 const u32x4 r1v = *reinterpret_cast<const u32x4*>(hp + 16 * (2 * u2 + 1));
-                if (kind == 1)  // left: [other >= a]
+                if constexpr (kind == 1)  // left: [other >= a]
                   af[u2] = (jo >= static_cast<int>(r0v[0]) ? 0x3F80u : 0u) |
                            (jo >= static_cast<int>(r1v[0]) ? 0x3F800000u : 0u);
                 else  // right: [other < e2]
                   af[u2] = (jo < static_cast<int>(r0v[3]) ? 0x3F80u : 0u) |
                            (jo < static_cast<int>(r1v[3]) ? 0x3F800000u : 0u);
               }
-              cc[kb2] = mfma_bf16(af, kind == 1 ? fl[ch] : fr[ch], cc[kb2]);
+              if constexpr (kind == 1) cc[kb2] = mfma_bf16(af, fl[ch], cc[kb2]);
+              else cc[kb2] = mfma_bf16(af, fr[ch], cc[kb2]);
             }
           }
         }
@@ -436,7 +582,11 @@ __global__ __launch_bounds__(NT, 1) void bwd_kernel(BwdArgs A, BwdOrder ord) {
         }
         (void)pf;
       }
-    }
+    };
+    int t = 0;
+    for (; t < nnear; ++t) tile(std::integral_constant<int, 0>{}, t);
+    for (; t < nnear + nleft; ++t) tile(std::integral_constant<int, 1>{}, t);
+    for (; t < ntl; ++t) tile(std::integral_constant<int, 2>{}, t);
   }
 
   // ---- epilogue: Acc1 is dQ^T or dK^T (times sqrt(d) too much), Acc2 dV^T
@@ -460,27 +610,32 @@ __global__ __launch_bounds__(NT, 1) void bwd_kernel(BwdArgs A, BwdOrder ord) {
   }
 }
 
-// D_r = <dO_r, O_r> for every (batch, query head, row): one wave per row
+// D_r = <dO_r, O_r> for every (batch, query head, row): D / 8 lanes per row,
+// 16-byte loads
 template <int D>
 __global__ __launch_bounds__(256) void rowdot_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
                                                      size_t rows, float* __restrict__ dd) {
-  const size_t r = static_cast<size_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (r >= rows) return;
+  constexpr int LPR = D / 8;  // lanes per row
+  const size_t r = static_cast<size_t>(blockIdx.x) * (256 / LPR) + threadIdx.x / LPR;
+  const int c = (threadIdx.x % LPR) * 8;
   float acc = 0.f;
-  for (int c = lane; c < D; c += 64) {
-    const float a = __uint_as_float(static_cast<uint32_t>(o[r * D + c]) << 16);
-    const float b = __uint_as_float(static_cast<uint32_t>(dout[r * D + c]) << 16);
-    acc = fmaf(a, b, acc);
+  if (r < rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(o + r * D + c);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(dout + r * D + c);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc = fmaf(__uint_as_float(a[k] << 16), __uint_as_float(b[k] << 16), acc);
+      acc = fmaf(__uint_as_float(a[k] & 0xFFFF0000u), __uint_as_float(b[k] & 0xFFFF0000u), acc);
+    }
   }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (lane == 0) dd[r] = acc;
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (r < rows && threadIdx.x % LPR == 0) dd[r] = acc;
 }
 
 template <int D, bool CAUSAL, int NCH, bool KEYSIDE>
 hipError_t launch_bwd_one(const BwdArgs& a, const BwdOrder& ord, int grid, hipStream_t st) {
-  constexpr int lds = 2 * BG<D>::STAGE + 16 * 128;
+  constexpr int lds = BG<D>::BIG + SMALL;
   auto kfn = bwd_kernel<D, CAUSAL, NCH, KEYSIDE>;
   static bool attr = false;  // benign race: idempotent
   if (lds > 64 * 1024 && !attr) {
@@ -517,10 +672,10 @@ hipError_t launch_plsh_bwd(const void* q, const void* k, const void* v, const vo
                            float* dd, hipStream_t st) {
   const size_t rows = static_cast<size_t>(batch) * hq * n;
   if (d == 64) {
-    hipLaunchKernelGGL(rowdot_kernel<64>, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, st,
+    hipLaunchKernelGGL(rowdot_kernel<64>, dim3(static_cast<unsigned>((rows + 31) / 32)), dim3(256), 0, st,
                        static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dout), rows, dd);
   } else {
-    hipLaunchKernelGGL(rowdot_kernel<128>, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, st,
+    hipLaunchKernelGGL(rowdot_kernel<128>, dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0, st,
                        static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dout), rows, dd);
   }
   hipError_t e = hipGetLastError();
