@@ -205,7 +205,7 @@ double tridiag_spectral(const std::vector<double>& a, const std::vector<double>&
 }
 
 struct ErrWorkspace {
-  size_t bins, scan, V, w, rowmax, h, part_v, part_i, scal, total;
+  size_t bins, scan, V, w, rowmax, h, part_v, part_i, scal, dots, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -231,6 +231,8 @@ ErrWorkspace err_workspace(int n, int s, int max_steps) {
   o = align256(o + 256 * sizeof(int));
   L.scal = o;
   o = align256(o + 8 * sizeof(double));
+  L.dots = o;
+  o = align256(o + plpsh::err_dots_bytes(max_steps + 1));
   L.total = o;
   return L;
 }
@@ -472,6 +474,7 @@ plpsh_status plpsh_error_norms(double sigma, int32_t n, int32_t s, const double*
   double* h1 = reinterpret_cast<double*>(ws + L.h);
   double* h2 = h1 + (max_steps + 1);
   double* scal = reinterpret_cast<double*>(ws + L.scal);
+  double* dpart = reinterpret_cast<double*>(ws + L.dots);
   const size_t ld = static_cast<size_t>(n);
 
   // max norm: row maxima, then the largest of them
@@ -511,11 +514,11 @@ plpsh_status plpsh_error_norms(double sigma, int32_t n, int32_t s, const double*
   for (k = 0; k < max_steps; ++k) {
     double* vk = V + k * ld;
     bool fail = hip_failed(plpsh::launch_err_matvec(plan, n, s, sigma, vk, w, ws + L.scan, st), "error product");
-    fail = fail || hip_failed(plpsh::launch_err_dots(V, ld, k + 1, w, n, h1, st), "dots") ||
+    fail = fail || hip_failed(plpsh::launch_err_dots(V, ld, k + 1, w, n, h1, dpart, st), "dots") ||
            hip_failed(plpsh::launch_err_sub_proj(V, ld, h1, k + 1, n, w, st), "projection") ||
-           hip_failed(plpsh::launch_err_dots(V, ld, k + 1, w, n, h2, st), "dots") ||
+           hip_failed(plpsh::launch_err_dots(V, ld, k + 1, w, n, h2, dpart, st), "dots") ||
            hip_failed(plpsh::launch_err_sub_proj(V, ld, h2, k + 1, n, w, st), "projection") ||
-           hip_failed(plpsh::launch_err_dots(w, ld, 1, w, n, scal + 2, st), "norm") ||
+           hip_failed(plpsh::launch_err_dots(w, ld, 1, w, n, scal + 2, dpart, st), "norm") ||
            hip_failed(hipMemcpyAsync(scal, h1 + k, sizeof(double), hipMemcpyDeviceToDevice, st), "copy") ||
            hip_failed(hipMemcpyAsync(scal + 1, h2 + k, sizeof(double), hipMemcpyDeviceToDevice, st), "copy") ||
            hip_failed(hipMemcpyAsync(host, scal, 8 * sizeof(double), hipMemcpyDeviceToHost, st), "copy") ||

@@ -18,6 +18,7 @@
 #include <algorithm>
 #include <cmath>
 
+#include "../../include/plpsh.h"
 #include "internal.h"
 
 namespace plpsh {
@@ -147,24 +148,34 @@ __global__ __launch_bounds__(kScanThreads) void scan_local_kernel(const double* 
   }
 }
 
-// Carries between tiles (one thread; a few hundred tiles at most):
-// car[3b] = P before tile b, car[3b+1] = F at the element before tile b,
-// car[3b+2] = G at the element after tile b.
-__global__ void scan_carry_kernel(const double* __restrict__ agg, int nb, double alpha_tile,
-                                  double* __restrict__ car) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  double cp = 0.0, cf = 0.0;
-  for (int b = 0; b < nb; ++b) {
-    car[3 * b + 0] = cp;
-    car[3 * b + 1] = cf;
-    cp += agg[3 * b + 0];
-    cf = agg[3 * b + 1] + alpha_tile * cf;
+// Carries between tiles: car[3b] = P before tile b, car[3b+1] = F at the
+// element before tile b, car[3b+2] = G at the element after tile b.  The
+// aggregates (at most 512 tiles) are staged in LDS by the whole block, then
+// chained by one thread.
+constexpr int kMaxScanTiles = PLPSH_MAX_N / kScanTile;
+__global__ __launch_bounds__(256) void scan_carry_kernel(const double* __restrict__ agg, int nb, double alpha_tile,
+                                                         double* __restrict__ car) {
+  __shared__ double sa[3 * kMaxScanTiles];
+  for (int i = threadIdx.x; i < 3 * nb; i += 256) sa[i] = agg[i];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double cp = 0.0, cf = 0.0;
+    for (int b = 0; b < nb; ++b) {
+      const double ap = sa[3 * b + 0], af = sa[3 * b + 1];
+      sa[3 * b + 0] = cp;
+      sa[3 * b + 1] = cf;
+      cp += ap;
+      cf = af + alpha_tile * cf;
+    }
+    double cg = 0.0;
+    for (int b = nb - 1; b >= 0; --b) {
+      const double ag = sa[3 * b + 2];
+      sa[3 * b + 2] = cg;
+      cg = ag + alpha_tile * cg;
+    }
   }
-  double cg = 0.0;
-  for (int b = nb - 1; b >= 0; --b) {
-    car[3 * b + 2] = cg;
-    cg = agg[3 * b + 2] + alpha_tile * cg;
-  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 3 * nb; i += 256) car[i] = sa[i];
 }
 
 __device__ __forceinline__ double prefix_incl(const double* pl, const double* car, int m) {
@@ -193,20 +204,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const double* __restrict__
   y[r] = lx - mx / static_cast<double>(s);
 }
 
-// out[j] = <V_j, w> for the m vectors V_j = V + j * ld (one workgroup each)
+// <V_j, w> for the m vectors V_j = V + j * ld: workgroup (j, k) sums rows
+// k, k + kDotSplit * 256, ... into part[j * kDotSplit + k]; a second pass adds
+// the parts of each j in a fixed order.
+constexpr int kDotSplit = 32;
 __global__ __launch_bounds__(256) void dots_kernel(const double* __restrict__ V, size_t ld, const double* __restrict__ w,
-                                                   int n, double* __restrict__ out) {
+                                                   int n, double* __restrict__ part) {
   __shared__ double red[256];
   const double* v = V + static_cast<size_t>(blockIdx.x) * ld;
   double acc = 0.0;
-  for (int r = threadIdx.x; r < n; r += 256) acc += v[r] * w[r];
+  for (int r = blockIdx.y * 256 + threadIdx.x; r < n; r += 256 * kDotSplit) acc += v[r] * w[r];
   red[threadIdx.x] = acc;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
     if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
     __syncthreads();
   }
-  if (threadIdx.x == 0) out[blockIdx.x] = red[0];
+  if (threadIdx.x == 0) part[blockIdx.x * kDotSplit + blockIdx.y] = red[0];
+}
+__global__ __launch_bounds__(256) void dots_sum_kernel(const double* __restrict__ part, int m,
+                                                       double* __restrict__ out) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= m) return;
+  double acc = 0.0;
+  for (int k = 0; k < kDotSplit; ++k) acc += part[j * kDotSplit + k];
+  out[j] = acc;
 }
 
 // w -= sum_{j<m} h[j] V_j
@@ -270,6 +292,8 @@ size_t err_scan_bytes(int n) {
   return (3 * static_cast<size_t>(n) + 6 * nb) * sizeof(double);
 }
 
+size_t err_dots_bytes(int m) { return static_cast<size_t>(m) * kDotSplit * sizeof(double); }
+
 hipError_t launch_err_rowmax(const PlanRec* plan, int n, int s, double sigma, double* rowmax, hipStream_t st) {
   const size_t lds = 2 * static_cast<size_t>(s) * kRowsPerBlock * sizeof(int);
   if (lds > 64 * 1024) {
@@ -297,13 +321,15 @@ hipError_t launch_err_matvec(const PlanRec* plan, int n, int s, double sigma, co
   const double alpha = std::exp(-1.0 / sigma);
   const double alpha_tile = std::exp(-static_cast<double>(kScanTile) / sigma);
   hipLaunchKernelGGL(scan_local_kernel, dim3(nb), dim3(kScanThreads), 0, st, x, n, alpha, pl, fl, gl, agg);
-  hipLaunchKernelGGL(scan_carry_kernel, dim3(1), dim3(64), 0, st, agg, nb, alpha_tile, car);
+  hipLaunchKernelGGL(scan_carry_kernel, dim3(1), dim3(256), 0, st, agg, nb, alpha_tile, car);
   hipLaunchKernelGGL(combine_kernel, dim3(cdiv(n, 256)), dim3(256), 0, st, x, plan, n, s, sigma, pl, fl, gl, car, y);
   return hipGetLastError();
 }
 
-hipError_t launch_err_dots(const double* V, size_t ld, int m, const double* w, int n, double* out, hipStream_t st) {
-  hipLaunchKernelGGL(dots_kernel, dim3(m), dim3(256), 0, st, V, ld, w, n, out);
+hipError_t launch_err_dots(const double* V, size_t ld, int m, const double* w, int n, double* out, double* part,
+                           hipStream_t st) {
+  hipLaunchKernelGGL(dots_kernel, dim3(m, kDotSplit), dim3(256), 0, st, V, ld, w, n, part);
+  hipLaunchKernelGGL(dots_sum_kernel, dim3(cdiv(m, 256)), dim3(256), 0, st, part, m, out);
   return hipGetLastError();
 }
 

@@ -50,7 +50,9 @@ size_t err_scan_bytes(int n);
 hipError_t launch_err_rowmax(const PlanRec* plan, int n, int s, double sigma, double* rowmax, hipStream_t st);
 hipError_t launch_err_matvec(const PlanRec* plan, int n, int s, double sigma, const double* x, double* y,
                              void* scratch, hipStream_t st);
-hipError_t launch_err_dots(const double* V, size_t ld, int m, const double* w, int n, double* out, hipStream_t st);
+size_t err_dots_bytes(int m);  // scratch of launch_err_dots for m vectors
+hipError_t launch_err_dots(const double* V, size_t ld, int m, const double* w, int n, double* out, double* part,
+                           hipStream_t st);
 hipError_t launch_err_sub_proj(const double* V, size_t ld, const double* h, int m, int n, double* w, hipStream_t st);
 hipError_t launch_err_scale(const double* w, double c, int n, double* v, hipStream_t st);
 hipError_t launch_err_argmax(const double* a, int n, double* pv, int* pi, double* out_v, int* out_i, hipStream_t st);
