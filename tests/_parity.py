@@ -72,3 +72,15 @@ def sample_rows(n, count, rng):
             base.add(t)
     extra = rng.choice(n, size=min(count, n), replace=False)
     return np.array(sorted(base.union(int(x) for x in extra)))
+
+
+def oracle_hashes(seed, sigmas, s, lib_delta=None, lib_u=None):
+    """The oracle's own draw of the hashes (its independent SplitMix64); when
+    the library's draw is given, it must be bit-identical.  Oracle inputs
+    never come from the library."""
+    d, u = oracle.sample_hashes(seed, sigmas, s)
+    if lib_delta is not None:
+        assert np.array_equal(np.asarray(lib_delta).reshape(d.shape), d), "library hash widths differ from the oracle's"
+        assert np.array_equal(np.asarray(lib_u).reshape(u.shape), u), "library hash offsets differ from the oracle's"
+    return d, u
+

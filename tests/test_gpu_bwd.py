@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 import synth
-from tests._parity import say, to64
+from tests._parity import oracle_hashes, say, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -62,9 +62,10 @@ def test_lse_and_gradients_match_oracle(gpu, case):
     B, Hq, Hkv, n, d, sig, s, causal = case
     say(f"backward case {case}")
     (q, k, v, do), (q64, k64, v64, do64) = _dev(B, Hq, Hkv, n, d, 40 + n, gpu)
-    delta, u, bins = P.sample_bins(17, sig, s, n, device=gpu)
-    o, lse = P.attention_lse(q, k, v, bins, causal=causal, delta=delta)
-    dq, dk, dv = P.attention_bwd(q, k, v, o, do, lse, bins, causal=causal, delta=delta)
+    ldelta, lu, bins = P.sample_bins(17, sig, s, n, device=gpu)
+    delta, u = oracle_hashes(17, sig, s, ldelta, lu)
+    o, lse = P.attention_lse(q, k, v, bins, causal=causal, delta=ldelta)
+    dq, dk, dv = P.attention_bwd(q, k, v, o, do, lse, bins, causal=causal, delta=ldelta)
     torch.cuda.synchronize()
     lse_ref = oracle.plsh_attention_lse(q64, k64, v64, delta, u, causal)
     assert np.abs(lse.double().cpu().numpy() - lse_ref).max() <= 1e-4 * max(1.0, np.abs(lse_ref).max())
@@ -80,9 +81,10 @@ def test_gradients_mid_size_full_compare(gpu):
     sig = synth.alibi_sigmas(Hq)
     say("backward mid size full compare")
     (q, k, v, do), (q64, k64, v64, do64) = _dev(B, Hq, Hkv, n, d, 77, gpu)
-    delta, u, bins = P.sample_bins(5, sig, s, n, device=gpu)
-    o, lse = P.attention_lse(q, k, v, bins, causal=True, delta=delta)
-    dq, dk, dv = P.attention_bwd(q, k, v, o, do, lse, bins, causal=True, delta=delta)
+    ldelta, lu, bins = P.sample_bins(5, sig, s, n, device=gpu)
+    delta, u = oracle_hashes(5, sig, s, ldelta, lu)
+    o, lse = P.attention_lse(q, k, v, bins, causal=True, delta=ldelta)
+    dq, dk, dv = P.attention_bwd(q, k, v, o, do, lse, bins, causal=True, delta=ldelta)
     torch.cuda.synchronize()
     gq, gk, gv = oracle.plsh_attention_grad(q64, k64, v64, do64, delta, u, True)
     say(f"  worst rel err dQ {_rel(to64(dq), gq, 'dQ'):.2e} dK {_rel(to64(dk), gk, 'dK'):.2e} "
@@ -122,12 +124,13 @@ def test_gradients_full_size(gpu):
     gen = torch.Generator(device=gpu)
     gen.manual_seed(9)
     do = torch.randn(q.shape, generator=gen, device=gpu, dtype=torch.float32).to(q.dtype)
-    delta, u, bins = P.sample_bins(W.hash_seed, W.sigmas, W.s, W.n, device=gpu)
-    o, lse = P.attention_lse(q, k, v, bins, causal=W.causal, delta=delta)
+    ldelta, lu, bins = P.sample_bins(W.hash_seed, W.sigmas, W.s, W.n, device=gpu)
+    delta, u = oracle_hashes(W.hash_seed, W.sigmas, W.s, ldelta, lu)
+    o, lse = P.attention_lse(q, k, v, bins, causal=W.causal, delta=ldelta)
     dq = torch.full_like(q, float("nan"))
     dk = torch.full_like(k, float("nan"))
     dv = torch.full_like(v, float("nan"))
-    P.attention_bwd(q, k, v, o, do, lse, bins, causal=W.causal, delta=delta, dq=dq, dk=dk, dv=dv)
+    P.attention_bwd(q, k, v, o, do, lse, bins, causal=W.causal, delta=ldelta, dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     for t in (dq, dk, dv):
         assert not torch.isnan(t).any().item(), "gradient not fully written"

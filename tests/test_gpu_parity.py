@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import synth
-from tests._parity import check_slices, oracle_full, sample_rows, say, to64
+from tests._parity import check_slices, oracle_full, oracle_hashes, sample_rows, say, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -90,10 +90,9 @@ def test_bins_bit_exact_edge_widths(gpu, n):
 def test_bins_bit_exact_workload_draws(gpu, name):
     W = synth.WORKLOADS[name]
     say(f"bins workload {name}")
-    delta, u, bins = P.sample_bins(W.hash_seed, W.sigmas, W.s, W.n, device=gpu)
+    ldelta, lu, bins = P.sample_bins(W.hash_seed, W.sigmas, W.s, W.n, device=gpu)
     torch.cuda.synchronize()
-    d2, u2 = oracle.sample_hashes(W.hash_seed, W.sigmas, W.s)
-    assert np.array_equal(delta, d2) and np.array_equal(u, u2)
+    delta, u = oracle_hashes(W.hash_seed, W.sigmas, W.s, ldelta, lu)
     heads = range(W.heads_q) if W.n <= 4096 else [0, 5, W.heads_q // 2, W.heads_q - 1]
     nblk = bins.nblk.cpu().numpy()
     starts = bins.starts.cpu().numpy()
@@ -130,7 +129,7 @@ def test_attention_matches_oracle_small(gpu, case):
     B, Hq, Hkv, n, d, dtype, sig, s, causal = case
     say(f"attention small case {case}")
     (q, k, v), (q64, k64, v64) = _qkv_dev(B, Hq, Hkv, n, d, dtype, 7 + n, gpu, scale_q=2.0)
-    delta, u = P.draw_hashes(11, sig, s)
+    delta, u = oracle_hashes(11, sig, s, *P.draw_hashes(11, sig, s))
     o = P.attention(q, k, v, sig, s, seed=11, causal=causal)
     torch.cuda.synchronize()
     ref = oracle_full(q64, k64, v64, delta, u, causal)
@@ -233,9 +232,10 @@ def test_literal_matches_literal_oracle(gpu, case):
     B, Hq, Hkv, n, d, dtype, sig, s, causal = case
     say(f"literal small case {case}")
     (q, k, v), (q64, k64, v64) = _qkv_dev(B, Hq, Hkv, n, d, dtype, 7 + n, gpu, scale_q=2.0)
-    delta, u, bins = P.sample_bins(11, sig, s, n, device=gpu)
+    ldelta, lu, bins = P.sample_bins(11, sig, s, n, device=gpu)
+    delta, u = oracle_hashes(11, sig, s, ldelta, lu)
     o = torch.full_like(q, float("nan"))
-    P.attention_literal(q, k, v, bins, causal=causal, delta=delta, out=o)
+    P.attention_literal(q, k, v, bins, causal=causal, delta=ldelta, out=o)
     torch.cuda.synchronize()
     ref = oracle.plsh_attention_literal(q64, k64, v64, delta, u, causal)
     err = check_slices(to64(o), ref, dtype, where=f"literal {case}")
@@ -246,9 +246,10 @@ def test_literal_full_size_sampled_rows(gpu):
     W = synth.WORKLOADS["mistral"]
     say("literal kernel, mistral full size, sampled rows")
     q, k, v = synth.qkv_torch(W.batch, W.heads_q, W.heads_kv, W.n, W.head_dim, W.dtype, W.data_seed, gpu)
-    delta, u, bins = P.sample_bins(W.hash_seed, W.sigmas, W.s, W.n, device=gpu)
+    ldelta, lu, bins = P.sample_bins(W.hash_seed, W.sigmas, W.s, W.n, device=gpu)
+    delta, u = oracle_hashes(W.hash_seed, W.sigmas, W.s, ldelta, lu)
     o = torch.full_like(q, float("nan"))
-    P.attention_literal(q, k, v, bins, causal=W.causal, delta=delta, out=o)
+    P.attention_literal(q, k, v, bins, causal=W.causal, delta=ldelta, out=o)
     torch.cuda.synchronize()
     assert not torch.isnan(o).any().item(), "output not fully written"
     rng = np.random.default_rng(9)
