@@ -123,6 +123,8 @@ plpsh_status check_qkv(const void* q, const void* k, const void* v, void* o, int
   if (d <= 0) return PLPSH_ERR_INVALID_ARGUMENT;
   if (d != 64 && d != 128) return PLPSH_ERR_UNSUPPORTED;
   if (n > PLPSH_MAX_N || hq > 1024 || batch > 65535) return PLPSH_ERR_UNSUPPORTED;
+  // the launches index (batch, head, 128-row tile) work items with 32-bit grids
+  if ((static_cast<long long>(n + 127) / 128 + 7) * batch * hq >= (1ll << 31)) return PLPSH_ERR_UNSUPPORTED;
   const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                        reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o);
   if (al & 15) return PLPSH_ERR_INVALID_ARGUMENT;

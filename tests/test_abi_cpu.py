@@ -104,6 +104,7 @@ def _attn(**kw):
     (dict(dtype=7), B.INVALID_ARGUMENT),
     (dict(d=96), B.UNSUPPORTED),
     (dict(d=0), B.INVALID_ARGUMENT),
+    (dict(batch=65535, n=B.MAX_N, hq=1024, hkv=1, sigma=np.full(1024, 2.0)), B.UNSUPPORTED),  # > 2^31 work items
     (dict(n=B.MAX_N + 1), B.UNSUPPORTED),
     (dict(wsb=10), B.WORKSPACE_TOO_SMALL),
     (dict(q=ctypes.c_void_p((1 << 20) + 4)), B.INVALID_ARGUMENT),        # misaligned
