@@ -262,9 +262,15 @@ def backward(P, W, run, flops_fwd, steps=10, warmup=3):
     f_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
     b_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
     tflops = 2.5 * flops_fwd / (b_ms * 1e-3) / 1e12
+    # algorithmic bytes: Q, O, dO, dQ (query-head sized), K, V, dK, dV (KV-head sized), LSE and D once each
+    qsz = W.batch * W.heads_q * W.n * W.head_dim * 2
+    kvsz = W.batch * W.heads_kv * W.n * W.head_dim * 2
+    bwd_bytes = 4 * qsz + 4 * kvsz + 2 * 4 * W.batch * W.heads_q * W.n
+    gbs = bwd_bytes / (b_ms * 1e-3) / 1e9
     return {"fwd_lse_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4), "bwd_over_fwd": round(b_ms / f_ms, 2),
             "train_tokens_per_s": round(W.batch * W.n / ((f_ms + b_ms) * 1e-3), 1),
-            "bwd_useful_tflops": round(tflops, 2), "bwd_mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+            "bwd_useful_tflops": round(tflops, 2), "bwd_mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "bwd_algorithmic_bytes": bwd_bytes, "bwd_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def fixed_blocks(P, W, q, k, v, steps=10, warmup=3):
