@@ -148,7 +148,7 @@ __device__ __forceinline__ void own_block(uint64_t lo64, uint64_t hi64, int a, i
 }
 
 template <int D, bool CAUSAL, int NCH, bool KEYSIDE>
-__global__ __launch_bounds__(NT, 1) void bwd_kernel(BwdArgs A, BwdOrder ord) {
+__global__ __launch_bounds__(NT, 2) void bwd_kernel(BwdArgs A, BwdOrder ord) {
   using G = BG<D>;
   using T = uint16_t;
   constexpr int KS = G::KS, DB = G::DB;
@@ -585,8 +585,10 @@ __global__ __launch_bounds__(NT, 1) void bwd_kernel(BwdArgs A, BwdOrder ord) {
     };
     int t = 0;
     for (; t < nnear; ++t) tile(std::integral_constant<int, 0>{}, t);
-    for (; t < nnear + nleft; ++t) tile(std::integral_constant<int, 1>{}, t);
-    for (; t < ntl; ++t) tile(std::integral_constant<int, 2>{}, t);
+    if constexpr (!CAUSAL || !KEYSIDE)  // other before own: dQ, or no causal cut
+      for (; t < nnear + nleft; ++t) tile(std::integral_constant<int, 1>{}, t);
+    if constexpr (!CAUSAL || KEYSIDE)   // other after own: dK/dV, or no causal cut
+      for (; t < ntl; ++t) tile(std::integral_constant<int, 2>{}, t);
   }
 
   // ---- epilogue: Acc1 is dQ^T or dK^T (times sqrt(d) too much), Acc2 dV^T
