@@ -386,7 +386,7 @@ plpsh_status plpsh_attention_fwd_lse(const void* q, const void* k, const void* v
                                      int32_t heads_q, int32_t heads_kv, int32_t n, int32_t head_dim,
                                      plpsh_dtype dtype, int32_t s, int32_t causal, const void* bins,
                                      size_t bins_bytes, const double* delta, void* stream) {
-  if (!lse && batch > 0 && n > 0) return PLPSH_ERR_INVALID_ARGUMENT;
+  if ((!lse && batch > 0 && n > 0) || (reinterpret_cast<uintptr_t>(lse) & 3)) return PLPSH_ERR_INVALID_ARGUMENT;
   return fwd_bins(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, s, causal, bins, bins_bytes, delta,
                   stream, false, lse);
 }
@@ -563,7 +563,8 @@ plpsh_status plpsh_attention_bwd(const void* q, const void* k, const void* v, co
   if (r != PLPSH_OK) return r;
   if (!valid_hs(heads_q, s)) return PLPSH_ERR_INVALID_ARGUMENT;
   if (batch == 0 || n == 0) return PLPSH_OK;
-  if (!o || !dout || !lse || !dk || !dv || !workspace || (reinterpret_cast<uintptr_t>(workspace) & 255))
+  if (!o || !dout || !lse || !dk || !dv || !workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3))
     return PLPSH_ERR_INVALID_ARGUMENT;
   for (const void* p : {o, dout, static_cast<const void*>(dk), static_cast<const void*>(dv)})
     if (reinterpret_cast<uintptr_t>(p) & 15) return PLPSH_ERR_INVALID_ARGUMENT;

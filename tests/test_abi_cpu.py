@@ -195,7 +195,7 @@ def test_backward_validation():
                                        a["causal"], a["bins"], a["binsb"], None, a["ws"], a["wsb"], None)
     for kw in [dict(lse=None), dict(do=None), dict(dk=None), dict(dv=None), dict(o=None), dict(ws=None),
                dict(ws=ctypes.c_void_p((1 << 20) + 16)), dict(do=ctypes.c_void_p((1 << 20) + 4)), dict(hkv=3),
-               dict(s=0), dict(causal=2), dict(bins=None)]:
+               dict(s=0), dict(causal=2), dict(bins=None), dict(lse=ctypes.c_void_p((1 << 20) + 2))]:
         assert call(**kw) == B.INVALID_ARGUMENT, kw
     assert call(dtype=0) == B.UNSUPPORTED
     assert call(d=80) == B.UNSUPPORTED
