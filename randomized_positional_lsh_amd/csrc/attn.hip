@@ -245,6 +245,7 @@ struct Fwd {
   float nbase[NRB][4];       // near counts at the key before each 32-position chunk of the tile
   float sc, scp, thr, beta;
   float Mrow[NRB], Msc[NRB], lsum[NRB];
+  bool started;               // wave-uniform: the running maximum has been raised once
   f32x4 acc[DB][NRB];
   u32x4 qb[NRB][BF ? KS : 1];
   float qf[NRB][BF ? 1 : KS];
@@ -377,8 +378,15 @@ struct Fwd {
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int J = jc + 16 * kb2 + 4 * g + e;
-            const bool ok = J >= lo_r[rb] && J < hi_r[rb];
+            bool ok;
+            if constexpr (PL) {
+              // the count is exactly 0 off the row's support and (causal)
+              // past the row itself, and at least 1 on it
+              ok = cacc[kb2][rb][e] > 0.5f;
+            } else {
+              const int J = jc + 16 * kb2 + 4 * g + e;
+              ok = J >= lo_r[rb] && J < hi_r[rb];
+            }
             sacc[kb2][rb][e] = ok ? sacc[kb2][rb][e] : -INFINITY;
           }
     }
@@ -393,15 +401,21 @@ struct Fwd {
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) grow = grow || lmx[rb] > Mrow[rb] + thr;
     if (__builtin_amdgcn_ballot_w64(grow)) {
+      // until the wave's first raise every maximum is -inf and every sum
+      // zero: that raise rescales nothing
+      const bool rescale = started;
+      started = true;
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
         const float mn = fmaxf(Mrow[rb], xmax16(lmx[rb]));
         const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((Mrow[rb] - mn) * scp);
         Mrow[rb] = mn;
         Msc[rb] = mn == -INFINITY ? 0.0f : mn * scp;
-        lsum[rb] *= alpha;
+        if (rescale) {
+          lsum[rb] *= alpha;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db][rb] *= alpha;
+          for (int db = 0; db < DB; ++db) acc[db][rb] *= alpha;
+        }
       }
     }
     // weights and the value product O^T += V^T P^T
@@ -527,9 +541,19 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
       const bool ok = (x == 0 || NCH == 4) && i < s;
       const PlanRec* ri = rec + (i < s ? i : 0);
       pb[x] = ok ? *reinterpret_cast<const u32x4*>(ri->bits) : u32x4{0, 0, 0, 0};
-      const u32x4 v = *reinterpret_cast<const u32x4*>(ri);
       // absent hashes: a = +inf, e = -inf, a2 = +inf, e2 = -inf (never count)
-      pr[x] = ok ? v : u32x4{0x7FFFFFFFu, 0x80000000u, 0x7FFFFFFFu, 0x80000000u};
+      if constexpr (CAUSAL && PL) {
+        // a and e only: the last row's block (a2, e2) bounds keys right of
+        // the tile, which causal rows never see.  (Loading the unused half
+        // lets the compiler reuse its registers, which then waits for the
+        // load before the query loads are issued.)
+        const u32x2 v = *reinterpret_cast<const u32x2*>(ri);
+        pr[x] = ok ? u32x4{v[0], v[1], 0x7FFFFFFFu, 0x80000000u}
+                   : u32x4{0x7FFFFFFFu, 0x80000000u, 0x7FFFFFFFu, 0x80000000u};
+      } else {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(ri);
+        pr[x] = ok ? v : u32x4{0x7FFFFFFFu, 0x80000000u, 0x7FFFFFFFu, 0x80000000u};
+      }
     }
   }
 
@@ -616,38 +640,51 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
             fhi = max(fhi, ei);
             continue;
           }
-          // row lane (first half)
-          const uint64_t m0 = lo64 & le, g0 = lo64 & ~le;
+          // row lane (first half), row 64 + lane (second half)
+          const uint64_t m0 = lo64 & le, m1 = hi64 & le;
           const int st0 = m0 ? 63 - __builtin_clzll(m0) : 0;
-          const int en0 = g0 ? __builtin_ctzll(g0) : (hi64 ? 64 + __builtin_ctzll(hi64) : BM);
-          // row 64 + lane (second half)
-          const uint64_t m1 = hi64 & le, g1 = hi64 & ~le;
           const int st1 = m1 ? 127 - __builtin_clzll(m1) : (lo64 ? 63 - __builtin_clzll(lo64) : 0);
-          const int en1 = g1 ? 64 + __builtin_ctzll(g1) : BM;
           lds_add(col0 + st0 * (2 * BM), onev);
-          lds_sub(col0 + en0 * (2 * BM), onev);
           lds_add(col1 + st1 * (2 * BM), onev);
-          lds_sub(col1 + en1 * (2 * BM), onev);
           lo0 = min(lo0, st0 ? r0 + st0 : ai);   // st = 0: the block of row r0
-          hi0 = max(hi0, en0 < BM ? r0 + en0 : ei);  // en = BM: the block of the last row
           lo1 = min(lo1, st1 ? r0 + st1 : ai);
-          hi1 = max(hi1, en1 < BM ? r0 + en1 : ei);
+          if constexpr (!CAUSAL) {
+            // the -1 at each block's end; causal rows instead end every
+            // block at the row itself (below), since keys past it are cut
+            const uint64_t g0 = lo64 & ~le, g1 = hi64 & ~le;
+            const int en0 = g0 ? __builtin_ctzll(g0) : (hi64 ? 64 + __builtin_ctzll(hi64) : BM);
+            const int en1 = g1 ? 64 + __builtin_ctzll(g1) : BM;
+            lds_sub(col0 + en0 * (2 * BM), onev);
+            lds_sub(col1 + en1 * (2 * BM), onev);
+            hi0 = max(hi0, en0 < BM ? r0 + en0 : ei);  // en = BM: the block of the last row
+            hi1 = max(hi1, en1 < BM ? r0 + en1 : ei);
+          }
         }
       }
       if (nfull > 0) {
         lds_add(col0, static_cast<uint32_t>(nfull) * onev);
         lds_add(col1, static_cast<uint32_t>(nfull) * onev);
       }
+      if constexpr (CAUSAL) {
+        // every block of row r ends after r, so with the keys past r cut the
+        // s blocks all end at r + 1 (row 127: the spare position 128)
+        if (w == NW - 1) {
+          lds_sub(col0 + (lane + 1) * (2 * BM), static_cast<uint32_t>(s) * onev);
+          lds_sub(col1 + (lane + 65) * (2 * BM), static_cast<uint32_t>(s) * onev);
+        }
+      }
       lo0 = min(lo0, flo);
       lo1 = min(lo1, flo);
-      hi0 = max(hi0, fhi);
-      hi1 = max(hi1, fhi);
       int* sLo = reinterpret_cast<int*>(sm + SM_LO);
-      int* sHi = reinterpret_cast<int*>(sm + SM_HI);
       __hip_atomic_fetch_min(sLo + lane, lo0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      __hip_atomic_fetch_max(sHi + lane, hi0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       __hip_atomic_fetch_min(sLo + 64 + lane, lo1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      __hip_atomic_fetch_max(sHi + 64 + lane, hi1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if constexpr (!CAUSAL) {
+        hi0 = max(hi0, fhi);
+        hi1 = max(hi1, fhi);
+        int* sHi = reinterpret_cast<int*>(sm + SM_HI);
+        __hip_atomic_fetch_max(sHi + lane, hi0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_max(sHi + 64 + lane, hi1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
     }
     // the hashes in two orders for the far tiles (waves with the fewest
     // hashes above): by the start a of the first row's block ascending, and
@@ -738,8 +775,9 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       f.lo_r[rb] = reinterpret_cast<const int*>(sm + SM_LO)[f.rr[rb]];
-      f.hi_r[rb] = reinterpret_cast<const int*>(sm + SM_HI)[f.rr[rb]];
-      if constexpr (CAUSAL) f.hi_r[rb] = min(f.hi_r[rb], f.R[rb] + 1);
+      // causal: every block of the row ends after it, so the cut at the row
+      // is the support's end
+      f.hi_r[rb] = CAUSAL ? min(f.R[rb] + 1, n) : reinterpret_cast<const int*>(sm + SM_HI)[f.rr[rb]];
     }
     {
       const int* sAa = reinterpret_cast<const int*>(sm + SM_SORT);
@@ -812,6 +850,7 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
   f.scp = MODE == MODE_ALIBI ? 1.0f : f.sc;        // scale applied at exp time
   f.thr = 8.0f / f.scp;                            // rescale margin (units of x)
   f.beta = MODE == MODE_ALIBI ? hsc.beta[h] : 0.0f;
+  f.started = false;
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     f.Mrow[rb] = -INFINITY;
