@@ -12,7 +12,8 @@ Prints ONE JSON line.  Besides the contract fields it carries:
   roofline     : the attention kernel against the HBM roofline (algorithmic
                  bytes = Q, K, V read once + O written once, per launch,
                  divided by the kernel's mean duration from HIP events
-                 recorded around it on its stream)
+                 recorded around it on its stream); also the same kernel
+                 with the L2 and last-level cache evicted before each launch
   cpu_baseline : the fp64 oracle timed on a bounded sample of the same
                  workload on the host cores
   dense_alibi  : exact ALiBi (plpsh_alibi_dense_fwd) at the same n
@@ -158,6 +159,24 @@ def time_steps(run, steps, warmup):
     wall = time.perf_counter() - t0
     kern = [a.elapsed_time(b) for a, b in ev]  # ms
     return wall, kern
+
+
+def cold_kernel_ms(run, reps=20):
+    """Mean attention-kernel time with the L2 and the 256 MB last-level
+    cache evicted before every launch: a 512 MiB buffer is overwritten on the
+    same stream between launches, outside the events."""
+    import numpy as np
+    import torch
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=run.q.device)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        scratch.fill_(1)
+        a.record()
+        run.attn()
+        b.record()
+    torch.cuda.synchronize()
+    del scratch
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
 def cpu_baseline(W, q, k, v, delta, u, seconds):
@@ -418,11 +437,15 @@ def main():
             traffic = int(tr["bytes_per_launch"])
     flops = useful_flops(W, P, run.ws)
     tflops = flops / (kern_ms * 1e-3) / 1e12
+    cold_ms = cold_kernel_ms(run)
+    log(f"attention kernel with caches evicted before each launch {cold_ms:.4f} ms")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "plpsh fwd_kernel (attention)", "kernel_ms": round(kern_ms, 5),
                 "algorithmic_bytes": abytes,
-                "useful_tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+                "useful_tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                "kernel_ms_cold_cache": round(cold_ms, 5),
+                "frac_cold_cache": round(abytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
