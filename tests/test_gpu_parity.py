@@ -118,6 +118,9 @@ CASES = [
     (1, 2, 1, 777, 128, "bf16", (5.0, 80.0), 32, False),
     (1, 2, 2, 300, 128, "bf16", (3.0, 50.0), 40, True),     # two count chunks
     (1, 2, 2, 300, 64, "bf16", (3.0, 50.0), 100, False),    # four count chunks
+    (1, 2, 2, 300, 64, "bf16", (3.0, 50.0), 100, True),
+    (1, 2, 1, 257, 128, "bf16", (0.6, 2.0), 128, True),      # s at its maximum; widths under 1
+    (1, 2, 1, 200, 64, "f32", (2.5, 40.0), 48, True),        # two count chunks, fp32
     (1, 2, 1, 1, 64, "bf16", (4.0, 8.0), 5, True),           # n = 1
     (1, 2, 1, 65, 128, "bf16", (4.0, 8.0), 5, True),
     (3, 2, 1, 129, 64, "f32", (0.5, 1000.0), 3, False),
@@ -221,7 +224,7 @@ def test_fixed_blocks(gpu):
         assert torch.equal(o, o2), f"fixed blocks vs one deterministic hash, causal={causal}"
 
 
-LITERAL_CASES = [CASES[i] for i in (0, 3, 4, 5, 6, 8, 9, 10, 11, 12)]
+LITERAL_CASES = [CASES[i] for i in (0, 3, 4, 5, 6, 8, 9, 10, 11, 13, 14, 15)]
 
 
 @pytest.mark.parametrize("case", LITERAL_CASES,
