@@ -240,7 +240,11 @@ __global__ __launch_bounds__(NT, 2) void bwd_kernel(BwdArgs A, BwdOrder ord) {
       const int i = lane + 64 * x;
       const bool ok = (x == 0 || NCH == 4) && i < s;
       const PlanRec* ri = rec + (i < s ? i : 0);
-      pb[x] = ok ? *reinterpret_cast<const u32x4*>(ri->bits) : u32x4{0, 0, 0, 0};
+      // both loads unconditional (ri is always a valid record): a load under
+      // a lane condition is merged by a wait for every load in flight,
+      // including the own-side operands issued just before
+      const u32x4 bv = *reinterpret_cast<const u32x4*>(ri->bits);
+      pb[x] = ok ? bv : u32x4{0, 0, 0, 0};
       const u32x4 v = *reinterpret_cast<const u32x4*>(ri);
       // absent hashes never count: a = +inf, e = -inf, a2 = +inf, e2 = -inf
       pr[x] = ok ? v : u32x4{0x7FFFFFFFu, 0x80000000u, 0x7FFFFFFFu, 0x80000000u};
