@@ -36,7 +36,12 @@
 //  * keys among the tile's own rows: c[r,j] = sum_{p <= j} H[r,p] where H
 //    counts hashes whose block of r starts at position p (clamped to r0)
 //    minus those whose block of r ends at p; summing over p <= j is a
-//    product with the constant matrix [p <= j] (K = 128 positions).
+//    product with the constant matrix [p <= j] (K = 128 positions).  With
+//    the causal cut every block of r ends at r + 1, so H holds -s there and
+//    the product gives c = 0 past the row.
+//
+// Masking: c is exactly 0 off a row's support (and, causal, past the row)
+// and at least 1 on it, so chunks that straddle a support edge mask on c.
 //
 // Softmax: one running row maximum shared by all hashes.  It is raised only
 // when a tile exceeds it by more than 2^8 in the exponential, so rescaling
@@ -611,10 +616,11 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
       // H[r][p] (stored [p][r], biased int16) by atomic adds: wave w takes the
       // hashes i = w mod NW for all 128 rows, rows lane and 64 + lane.  For
       // row r and hash i, +1 at the start of the block of r (0 when it starts
-      // before the tile) and -1 at its end (the spare row 128 when past the
-      // tile).  The boundary bits are wave-uniform, so every branch here is
-      // scalar.  The same pass gives each row its support [lo, hi): the least
-      // block start and the greatest block end over the hashes.
+      // before the tile) and, not causal, -1 at its end (the spare row 128
+      // when past the tile).  The boundary bits are wave-uniform, so every
+      // branch here is scalar.  The same pass gives each row its support
+      // [lo, hi): the least block start and the greatest block end over the
+      // hashes (causal: the row itself ends it).
       const uint64_t le = lane == 63 ? ~0ull : ((2ull << lane) - 1);  // bits <= lane
       unsigned char* col0 = hc + 2 * (lane - (lane & 1));
       unsigned char* col1 = col0 + 2 * 64;
