@@ -25,26 +25,53 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
+// Bin of position x from the product with a rounded reciprocal, which is
+// within 2.2 ulp of the quotient: where no integer lies within 2^-50 |q| of
+// it the floor equals that of the correctly rounded quotient, and the
+// function returns true (certified).
+__device__ __forceinline__ bool certified_bin(int x, double u, double rinv, double* f) {
+  const double q = (static_cast<double>(x) - u) * rinv;
+  const double fl = floor(q);
+  const double fr = q - fl;  // exact for |q| < 2^52
+  const double margin = fabs(q) * 0x1p-50;
+  *f = fl;
+  return fr > margin && fr < 1.0 - margin;
+}
+
 // Start flags of the 32 positions x0 .. x0 + 31 (bit b: bin(x0 + b) differs
 // from bin(x0 + b - 1)), bins evaluated in binary64 as floor((x - u) / delta).
-// First from the product with a rounded reciprocal, which is within 2.2 ulp
-// of the quotient: where no integer lies within 2^-50 |q| of it the floor
-// equals that of the correctly rounded quotient.  If any of the 33 positions
-// misses that margin (rare) the word is redone with the division itself.
-// The fast pass is fully unrolled so that the evaluations overlap.
-__device__ __forceinline__ uint32_t start_flags(int x0, double u, double delta, double rinv) {
+//
+// Wide hashes (delta >= 32, the same for the whole workgroup, so the branch
+// does not diverge): computed bins never decrease with x (the rounded
+// subtraction and division are monotone), and the bins of x0 - 1 and
+// x0 + 31 differ by at most one.  Equal bins mean no start in the word;
+// bins one apart mean exactly one start, found by bisection (5 more
+// evaluations).  Everything else, and any evaluation that is not
+// certified, takes the general pass: all 33 bins by certified products,
+// and if one of them misses the margin (rare), the division itself.
+// The general pass is fully unrolled so that the evaluations overlap.
+__device__ __forceinline__ uint32_t start_flags(int x0, double u, double delta, double rinv, bool wide) {
+  if (wide) {
+    double fa, fb;
+    bool ok = certified_bin(x0 - 1, u, rinv, &fa);
+    ok = certified_bin(x0 + 31, u, rinv, &fb) && ok;
+    if (ok && fa == fb) return 0u;
+    if (ok && fb == fa + 1.0) {
+      int lo = -1, hi = 31;  // bin(x0 + lo) = fa, bin(x0 + hi) = fb
+#pragma unroll
+      for (int it = 0; it < 5; ++it) {
+        const int mid = (lo + hi) >> 1;
+        double fm;
+        ok = certified_bin(x0 + mid, u, rinv, &fm) && ok;
+        if (fm == fb) hi = mid; else lo = mid;
+      }
+      if (ok) return 1u << hi;
+    }
+  }
   double f[33];
   bool exact = false;
 #pragma unroll
-  for (int k = 0; k < 33; ++k) {
-    const double d = static_cast<double>(x0 - 1 + k) - u;
-    const double q = d * rinv;
-    const double fl = floor(q);
-    const double fr = q - fl;  // exact for |q| < 2^52
-    const double margin = fabs(q) * 0x1p-50;
-    f[k] = fl;
-    exact = exact || !(fr > margin && fr < 1.0 - margin);
-  }
+  for (int k = 0; k < 33; ++k) exact = !certified_bin(x0 - 1 + k, u, rinv, &f[k]) || exact;
   uint32_t m = 0u;
   if (!exact) {
 #pragma unroll
@@ -86,9 +113,9 @@ __global__ __launch_bounds__(kThreads) void bins_kernel(const double* __restrict
                                                         int32_t* __restrict__ nblk,
                                                         int32_t* __restrict__ starts,
                                                         PlanRec* __restrict__ plan) {
-  extern __shared__ uint32_t lds[];
-  uint32_t* bits = lds;                                   // [nwords] start bitmap
-  int32_t* pre = reinterpret_cast<int32_t*>(lds + nwords);  // [nwords] starts before word
+  // per 32-position word: its start bitmap (x) and the number of block
+  // starts before it (y), side by side so that one 8-byte read gets both
+  extern __shared__ uint2 wd[];
   __shared__ int wsum[kWaves];
 
   const int hid = blockIdx.x;  // hash index h * s + i
@@ -96,6 +123,7 @@ __global__ __launch_bounds__(kThreads) void bins_kernel(const double* __restrict
   const int tid = threadIdx.x;
   const double delta = du[2 * hid], u = du[2 * hid + 1];
   const double rinv = 1.0 / delta;
+  const bool wide = delta >= 32.0;
 
   // block starts: bit x of the map is set iff x = 0 or bin(x) != bin(x - 1)
   // (one 32-position word per thread and step; words past n stay zero)
@@ -104,11 +132,11 @@ __global__ __launch_bounds__(kThreads) void bins_kernel(const double* __restrict
     uint32_t m = 0u;
     if (w < nused) {
       const int x0 = 32 * w;
-      m = start_flags(x0, u, delta, rinv);
+      m = start_flags(x0, u, delta, rinv, wide);
       if (x0 == 0) m |= 1u;
       if (n - x0 < 32) m &= (1u << (n - x0)) - 1u;
     }
-    bits[w] = m;
+    wd[w].x = m;
   }
   __syncthreads();
 
@@ -116,28 +144,47 @@ __global__ __launch_bounds__(kThreads) void bins_kernel(const double* __restrict
   const int per = (nwords + kThreads - 1) / kThreads;
   const int w0 = tid * per, w1 = min(w0 + per, nwords);
   int local = 0;
-  for (int w = w0; w < w1; ++w) local += __popc(bits[w]);
+  for (int w = w0; w < w1; ++w) local += __popc(wd[w].x);
   int total;
   int base = wg_exclusive_scan(local, wsum, &total);
   for (int w = w0; w < w1; ++w) {
-    pre[w] = base;
-    base += __popc(bits[w]);
+    const uint32_t m = wd[w].x;
+    wd[w].y = static_cast<uint32_t>(base);
+    base += __popc(m);
   }
   __syncthreads();
 
   int32_t* st = starts + static_cast<size_t>(hid) * (n + 1);
   if (delta < 4.0) {
-    // dense: one position per thread, consecutive threads write consecutive starts
-#pragma unroll 4
-    for (int x = tid; x < n; x += kThreads) {
-      const uint32_t m = bits[x >> 5];  // both reads unconditional, so unrolled steps overlap
-      const int o = pre[x >> 5] + __popc(m & ((1u << (x & 31)) - 1u));
-      if ((m >> (x & 31)) & 1u) st[o] = x;
+    // dense: one position per thread, consecutive threads write consecutive
+    // starts.  Four positions per thread and step: the four words (bitmap and
+    // offset in one read each; indices clamped into the array, the stores
+    // guarded) are read before any store, and the offsets are pinned in
+    // registers there, so the compiler cannot move the reads into the store
+    // branches, which would serialise one LDS round trip per position.
+    const int last = nwords - 1;
+    for (int x0 = tid; x0 < n; x0 += 4 * kThreads) {
+      uint2 e[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) e[k] = wd[min((x0 + k * kThreads) >> 5, last)];
+      int o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int x = x0 + k * kThreads;
+        o[k] = static_cast<int>(e[k].y) + __popc(e[k].x & ((1u << (x & 31)) - 1u));
+        asm volatile("" : "+v"(o[k]));
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int x = x0 + k * kThreads;
+        if (x < n && ((e[k].x >> (x & 31)) & 1u)) st[o[k]] = x;
+      }
     }
   } else {
     for (int w = tid; w < nused; w += kThreads) {
-      uint32_t m = bits[w];
-      int b = pre[w];
+      const uint2 e = wd[w];
+      uint32_t m = e.x;
+      int b = static_cast<int>(e.y);
       while (m) {
         st[b++] = (w << 5) + (__ffs(m) - 1);
         m &= m - 1;
@@ -157,15 +204,16 @@ __global__ __launch_bounds__(kThreads) void bins_kernel(const double* __restrict
     const int r0 = q * kPlanTile;
     const int rl = min(r0 + kPlanTile - 1, n - 1);
     const int x0w = r0 >> 5, xlw = rl >> 5;
-    const int kb0 = pre[x0w] + __popc(bits[x0w] & (0xFFFFFFFFu >> (31 - (r0 & 31)))) - 1;
-    const int kbl = pre[xlw] + __popc(bits[xlw] & (0xFFFFFFFFu >> (31 - (rl & 31)))) - 1;
+    const uint2 e0 = wd[x0w], el = wd[xlw];
+    const int kb0 = static_cast<int>(e0.y) + __popc(e0.x & (0xFFFFFFFFu >> (31 - (r0 & 31)))) - 1;
+    const int kbl = static_cast<int>(el.y) + __popc(el.x & (0xFFFFFFFFu >> (31 - (rl & 31)))) - 1;
     PlanRec rec;
     rec.a = st[kb0];
     rec.e = st[kb0 + 1];
     rec.a2 = st[kbl];
     rec.e2 = st[kbl + 1];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) rec.bits[j] = bits[x0w + j];
+    for (int j = 0; j < 4; ++j) rec.bits[j] = wd[x0w + j].x;
     rec.bits[0] &= ~1u;
     if (n - r0 < kPlanTile) {
       const int p = n - r0;

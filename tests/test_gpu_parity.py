@@ -86,6 +86,31 @@ def test_bins_bit_exact_edge_widths(gpu, n):
     _check_bins(bins, delta, u, n)
 
 
+@pytest.mark.parametrize("n", [4097, 16384])
+def test_bins_bit_exact_wide_hashes(gpu, n):
+    """Widths of 32 and more, where the device settles most 32-position words
+    from the bins at their two ends and finds a single start by bisection:
+    starts on the first and the last position of a word (delta = 32 with
+    u = 0 or 1), widths just above 32, offsets at the ends of [0, delta),
+    and random wide draws, every block checked against the oracle."""
+    rng = np.random.default_rng(77 + n)
+    delta, u = [], []
+    for w in (32.0, 32.0 + 2 ** -40, 33.3, 64.0, 100.5, 256.0, 1000.0, 4096.0, 5000.25):
+        for uu in (0.0, 1.0, 15.5, 31.0, w / 2, w * (1 - 2 ** -30), rng.uniform(0, w), rng.uniform(0, w)):
+            delta.append(w)
+            u.append(min(uu, w))
+    wr = 32.0 + rng.gamma(2.0, 200.0, size=64)
+    delta += wr.tolist()
+    u += (wr * rng.uniform(size=64)).tolist()
+    s = 8
+    delta = np.array(delta).reshape(-1, s)
+    u = np.array(u).reshape(-1, s)
+    say(f"bins wide hashes n={n} hashes={delta.size}")
+    bins = P.bins_from_hashes(delta, u, n, device=gpu)
+    torch.cuda.synchronize()
+    _check_bins(bins, delta, u, n)
+
+
 @pytest.mark.parametrize("name", ["tiny", "small", "qwen3", "mistral"])
 def test_bins_bit_exact_workload_draws(gpu, name):
     W = synth.WORKLOADS[name]
