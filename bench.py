@@ -27,7 +27,10 @@ Prints ONE JSON line.  Besides the contract fields it carries:
                  counted pair against the forward's 2)
   fixed_blocks : the deterministic fixed-blocks baseline (plpsh_fixed_blocks_fwd,
                  block b_h = round(2 sigma_h), the mean of Gamma(2, sigma_h))
-  crossover    : PLSH vs dense ALiBi step times over n (Mistral shape)
+  crossover    : PLSH vs dense ALiBi step times over n = 512 .. 131072
+                 (Mistral shape, s = 20)
+  long_context : the long-context workload (n = 131072, s = 32) as a step,
+                 against dense ALiBi at the same n
   convergence  : ||L* - M~||_2 and ||L* - M~||_max against s at n = 131072,
                  sigma = 256 (plpsh_error_norms), with the fitted log-log
                  slopes and the time per measurement
@@ -333,6 +336,28 @@ def crossover(P, synth, dev, ns, steps=5):
     return out
 
 
+def long_point(P, synth, dev, dense_ms, steps=5):
+    """The long-context workload (n = 131072, s = 32, causal, Mistral head
+    layout) as one step of the whole path, against dense exact ALiBi at the
+    same n (the dense kernel does not depend on s)."""
+    import torch
+    W = synth.WORKLOADS["long"]
+    q, k, v = synth.qkv_torch(W.batch, W.heads_q, W.heads_kv, W.n, W.head_dim, W.dtype, W.data_seed, dev)
+    run = Runner(P, W, q, k, v, torch.empty_like(q), dev)
+    wall, kern = time_steps(run, steps, 2)
+    ms = 1e3 * wall / steps
+    del q, k, v, run
+    torch.cuda.empty_cache()
+    kms = sum(kern) / len(kern)
+    out = {"workload": "long-context", "n": W.n, "s": W.s, "plsh_ms": round(ms, 4),
+           "kernel_ms": round(kms, 4), "tokens_per_s": round(W.batch * W.n / (ms * 1e-3), 1),
+           "hbm_frac": round(algorithmic_bytes(W) / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if dense_ms is not None:
+        out["dense_ms"] = round(dense_ms, 4)
+        out["speedup_plsh_vs_dense"] = round(dense_ms / ms, 2)
+    return out
+
+
 def convergence(P, dev, n=131072, sigma=256.0, ss=(2, 4, 8, 16, 32, 64, 128), seeds=3, max_steps=400):
     """Both error norms of the mask mean against L* over s, one head."""
     import numpy as np
@@ -476,8 +501,11 @@ def main():
         log(f"fixed blocks {fms:.4f} ms")
     if not args.no_crossover and W.name == "mistral":
         del o
-        line["crossover"] = crossover(P, synth, dev, [512, 1024, 2048, 4096, 8192, 16384, 32768, 65536])
+        line["crossover"] = crossover(P, synth, dev, [512, 1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072])
         log(f"crossover {line['crossover']}")
+        cx = line["crossover"]
+        line["long_context"] = long_point(P, synth, dev, cx["dense_ms"][-1] if cx["n"][-1] == 131072 else None)
+        log(f"long context {line['long_context']}")
     if not args.no_convergence:
         line["convergence"] = convergence(P, dev)
         log(f"convergence {line['convergence']}")
