@@ -5,6 +5,12 @@
       --kernel-trace --stats CSV in DIR for the kernels of this library,
       labelled by kernel and template instance.
 
+  python -m randomized_positional_lsh_amd.profsum util DIR OUT.md --cmd "..."
+      Unit utilisation of the count-weighted attention kernel from one --pmc
+      pass of GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES, SQ_ACTIVE_INST_VALU,
+      SQ_LDS_IDX_ACTIVE and SQ_LDS_BANK_CONFLICT (means over its dispatches;
+      GRBM_GUI_ACTIVE summed over the 8 XCDs, so divided by 8 for cycles).
+
   python -m randomized_positional_lsh_amd.profsum traffic FETCH WRITE CFETCH CWRITE OUT.json \
           --workload mistral --kernel-sha SHA --copy-bytes N --cmd "..."
       HBM bytes per launch of the count-weighted attention kernel at the
@@ -83,6 +89,36 @@ def stats(d: str, out: str, cmd: str) -> None:
     print("\n".join(lines))
 
 
+def util(d: str, out: str, cmd: str, cus: int = 256, simds: int = 1024, xcds: int = 8) -> None:
+    path = _one(os.path.join(d, "**", "*counter_collection.csv"))
+    per: dict = {}
+    for r in csv.DictReader(open(path)):
+        if MAIN in r["Kernel_Name"]:
+            per.setdefault(r["Dispatch_Id"], {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    need = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_LDS_IDX_ACTIVE",
+            "SQ_LDS_BANK_CONFLICT")
+    rows = [v for v in per.values() if all(k in v for k in need)]
+    if not rows:
+        raise ValueError(f"no dispatches of {MAIN} with counters {need} in {path}")
+    m = {k: statistics.mean(v[k] for v in rows) for k in need}
+    cyc = m["GRBM_GUI_ACTIVE"] / xcds
+    res = [
+        ("matrix cores busy (SQ_VALU_MFMA_BUSY_CYCLES / (cycles x SIMDs))", m["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * simds)),
+        ("vector ALU instructions active (4 x SQ_ACTIVE_INST_VALU / (cycles x SIMDs))",
+         4 * m["SQ_ACTIVE_INST_VALU"] / (cyc * simds)),
+        ("LDS busy (SQ_LDS_IDX_ACTIVE / (cycles x CUs))", m["SQ_LDS_IDX_ACTIVE"] / (cyc * cus)),
+        ("LDS bank-conflict stalls (SQ_LDS_BANK_CONFLICT / (cycles x CUs))", m["SQ_LDS_BANK_CONFLICT"] / (cyc * cus)),
+    ]
+    lines = ["# Unit utilisation of the attention kernel", "", f"Command: `{cmd}`", "",
+             f"Kernel: {MAIN}, {len(rows)} dispatches; cycles per dispatch (GRBM_GUI_ACTIVE / {xcds}): {cyc:.0f}.",
+             "", "| unit | share of cycles |", "|---|---|"]
+    lines += [f"| {name} | {100 * v:.1f}% |" for name, v in res]
+    lines += ["", f"Source: {os.path.basename(path)} (rocprofv3 --pmc, counters per dispatch)."]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def _counter_kib(d: str, regex_part: str, counter: str) -> list[float]:
     path = _one(os.path.join(d, "**", "*counter_collection.csv"))
     per = {}
@@ -120,6 +156,10 @@ def main() -> None:
     a.add_argument("dir")
     a.add_argument("out")
     a.add_argument("--cmd", required=True)
+    c = sub.add_parser("util")
+    c.add_argument("dir")
+    c.add_argument("out")
+    c.add_argument("--cmd", required=True)
     b = sub.add_parser("traffic")
     for x in ("fetch", "write", "cfetch", "cwrite", "out"):
         b.add_argument(x)
@@ -130,6 +170,8 @@ def main() -> None:
     args = ap.parse_args()
     if args.cmd_name == "stats":
         stats(args.dir, args.out, args.cmd)
+    elif args.cmd_name == "util":
+        util(args.dir, args.out, args.cmd)
     else:
         traffic(args.fetch, args.write, args.cfetch, args.cwrite, args.out, args.workload, args.kernel_sha,
                 args.copy_bytes, args.cmd)
