@@ -12,8 +12,9 @@ Prints ONE JSON line.  Besides the contract fields it carries:
   roofline     : the attention kernel against the HBM roofline (algorithmic
                  bytes = Q, K, V read once + O written once, per launch,
                  divided by the kernel's mean duration from HIP events
-                 recorded around it on its stream); also the same kernel
-                 with the L2 and last-level cache evicted before each launch
+                 recorded around it on its stream in 10 evenly spaced steps
+                 of the timed loop); also the same kernel with the L2 and
+                 last-level cache evicted before each launch
   cpu_baseline : the fp64 oracle timed on a bounded sample of the same
                  workload on the host cores
   dense_alibi  : exact ALiBi (plpsh_alibi_dense_fwd) at the same n
@@ -144,23 +145,35 @@ class Runner:
             raise RuntimeError(self.P.status_string(st))
 
 
-def time_steps(run, steps, warmup):
+def time_steps(run, steps, warmup, samples=10):
+    """Wall time of `steps` back-to-back steps, and the attention kernel's
+    duration (ms) from HIP events recorded around it on its stream in
+    `samples` evenly spaced steps of the same timed loop (all steps if
+    samples >= steps, none if 0).  An event pair between the two kernels of
+    a step costs the stream about 7 us on MI355X, so recording one in every
+    step would add that much to every step's time."""
     import torch
     for _ in range(warmup):
         run.bins()
         run.attn()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    every = 0 if samples <= 0 else max(1, steps // samples)
+    marks = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for i in range(steps) if every and i % every == 0}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for a, b in ev:
+    for i in range(steps):
         run.bins()
-        a.record()
-        run.attn()
-        b.record()
+        ab = marks.get(i)
+        if ab is None:
+            run.attn()
+        else:
+            ab[0].record()
+            run.attn()
+            ab[1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern = [a.elapsed_time(b) for a, b in ev]  # ms
+    kern = [a.elapsed_time(b) for a, b in marks.values()]  # ms
     return wall, kern
 
 
@@ -320,7 +333,7 @@ def crossover(P, synth, dev, ns, steps=5):
         W = synth.Workload(f"mistral-n{n}", 1, 32, 8, n, 128, "bf16", synth.alibi_sigmas(32), 20, True, 0, 1003)
         q, k, v = synth.qkv_torch(1, 32, 8, n, 128, "bf16", 1003, dev)
         run = Runner(P, W, q, k, v, torch.empty_like(q), dev)
-        wall, _ = time_steps(run, steps, 2)
+        wall, _ = time_steps(run, steps, 2, samples=0)
         dms = dense_alibi(P, W, q, k, v, steps=steps, warmup=2)
         out["n"].append(n)
         out["plsh_ms"].append(round(1e3 * wall / steps, 4))
@@ -344,7 +357,7 @@ def long_point(P, synth, dev, dense_ms, steps=5):
     W = synth.WORKLOADS["long"]
     q, k, v = synth.qkv_torch(W.batch, W.heads_q, W.heads_kv, W.n, W.head_dim, W.dtype, W.data_seed, dev)
     run = Runner(P, W, q, k, v, torch.empty_like(q), dev)
-    wall, kern = time_steps(run, steps, 2)
+    wall, kern = time_steps(run, steps, 2, samples=steps)
     ms = 1e3 * wall / steps
     del q, k, v, run
     torch.cuda.empty_cache()
