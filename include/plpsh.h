@@ -299,7 +299,12 @@ size_t plpsh_attention_bwd_workspace_bytes(int32_t batch, int32_t heads_q, int32
  *                plpsh_attention_bwd_workspace_bytes(batch, heads_q, n).
  * bf16 only (PLPSH_ERR_UNSUPPORTED for f32); head_dim 64 or 128.  Arithmetic:
  * bf16 products on the matrix cores with fp32 accumulation; P and dS are
- * rounded to bf16 before their products.  Asynchronous on `stream`.
+ * rounded to bf16 before their products.  Asynchronous on `stream`: the dK/dV
+ * kernel runs on a second stream of the device (created on first use, default
+ * priority, kept until the process ends) beside the dQ kernel, forked from and
+ * joined back to `stream` with events, so work issued to `stream` afterwards
+ * sees all three gradients.  Calls from several threads are serialised around
+ * that fork and join.
  */
 plpsh_status plpsh_attention_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                                  const float* lse, void* dq, void* dk, void* dv, int32_t batch, int32_t heads_q,

@@ -24,6 +24,7 @@
 // symmetric, so both directions use the same formulas.  With GQA the dK/dV
 // workgroup sums over the query heads of its KV head.
 #include <climits>
+#include <mutex>
 #include <type_traits>
 
 #include "internal.h"
@@ -670,6 +671,15 @@ hipError_t launch_bwd_dir(const BwdArgs& a, const BwdOrder& o, int d, int causal
   return hipErrorInvalidValue;
 }
 
+// per device: the second stream of the backward pass and its fork/join events
+constexpr int kSideDevices = 64;
+struct SideStream {
+  std::mutex mu;
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+SideStream g_side[kSideDevices];
+
 }  // namespace
 
 hipError_t launch_plsh_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -697,9 +707,29 @@ hipError_t launch_plsh_bwd(const void* q, const void* k, const void* v, const vo
   BwdOrder oq{}, okv{};
   for (int i = 0; i < hq; ++i) oq.w[i >> 1] |= static_cast<uint32_t>(head_order[i]) << (16 * (i & 1));
   for (int i = 0; i < hkv; ++i) okv.w[i >> 1] |= static_cast<uint32_t>(kv_order[i]) << (16 * (i & 1));
+  // dK/dV on a second stream of the device, beside dQ on the caller's stream
+  // (both read the same inputs and D, and write different outputs), so that
+  // each kernel fills the other's tail; joined back to the caller's stream.
+  int dev = 0;
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kSideDevices) return hipErrorInvalidDevice;
+  SideStream& side = g_side[dev];
+  std::lock_guard<std::mutex> lock(side.mu);
+  if (side.s == nullptr) {
+    // default priority (the only one used anywhere in this library)
+    if ((e = hipStreamCreateWithFlags(&side.s, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&side.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&side.join, hipEventDisableTiming)) != hipSuccess) return e;
+  }
+  if ((e = hipEventRecord(side.fork, st)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(side.s, side.fork, 0)) != hipSuccess) return e;
+  e = launch_bwd_dir<true>(a, okv, d, causal, 8 * a.cs * batch * hkv, side.s);
+  if (e != hipSuccess) return e;
+  if ((e = hipEventRecord(side.join, side.s)) != hipSuccess) return e;
   e = launch_bwd_dir<false>(a, oq, d, causal, 8 * a.cs * batch * hq, st);
   if (e != hipSuccess) return e;
-  return launch_bwd_dir<true>(a, okv, d, causal, 8 * a.cs * batch * hkv, st);
+  return hipStreamWaitEvent(st, side.join, 0);
 }
 
 }  // namespace plpsh

@@ -151,3 +151,32 @@ def test_gradients_full_size(gpu):
     dk_sum = dk.double().sum(dim=2)[0]
     dk_scale = dk.double().abs().sum(dim=2)[0]
     assert (dk_sum.abs() <= 2e-2 * dk_scale + 1e-6).all().item()
+
+
+def test_gradients_ordered_on_the_callers_stream(gpu):
+    """The dK/dV kernel runs on a second stream of the device, forked from and
+    joined back to the caller's stream: copies enqueued on the caller's
+    (non-default) stream right after the call, with no device-wide
+    synchronisation, must see every gradient, bit-identical to a call on the
+    default stream.  The outputs are filled with NaN before each call."""
+    B, Hq, Hkv, n, d, s = 1, 8, 2, 2048, 128, 20
+    sig = synth.alibi_sigmas(Hq)
+    say("backward ordering on a side stream")
+    (q, k, v, do), _ = _dev(B, Hq, Hkv, n, d, 91, gpu)
+    ldelta, lu, bins = P.sample_bins(3, sig, s, n, device=gpu)
+    o, lse = P.attention_lse(q, k, v, bins, causal=True, delta=ldelta)
+    ref = P.attention_bwd(q, k, v, o, do, lse, bins, causal=True, delta=ldelta)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in ref]
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        got = []
+        for _ in range(3):
+            dq, dk, dv = (torch.full_like(t, float("nan")) for t in ref)
+            P.attention_bwd(q, k, v, o, do, lse, bins, causal=True, delta=ldelta, dq=dq, dk=dk, dv=dv, stream=st)
+            got.append([t.clone() for t in (dq, dk, dv)])
+    st.synchronize()
+    for copies in got:
+        for g, want in zip(copies, ref):
+            assert torch.equal(g, want)
