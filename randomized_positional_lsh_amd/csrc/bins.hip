@@ -22,7 +22,7 @@
 namespace plpsh {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 
 // Bin of position x from the product with a rounded reciprocal, which is
