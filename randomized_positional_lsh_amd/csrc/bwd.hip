@@ -675,6 +675,7 @@ hipError_t launch_bwd_dir(const BwdArgs& a, const BwdOrder& o, int d, int causal
 constexpr int kSideDevices = 64;
 struct SideStream {
   std::mutex mu;
+  bool ready = false;  // all three created
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
 };
@@ -716,11 +717,22 @@ hipError_t launch_plsh_bwd(const void* q, const void* k, const void* v, const vo
   if (dev < 0 || dev >= kSideDevices) return hipErrorInvalidDevice;
   SideStream& side = g_side[dev];
   std::lock_guard<std::mutex> lock(side.mu);
-  if (side.s == nullptr) {
-    // default priority (the only one used anywhere in this library)
-    if ((e = hipStreamCreateWithFlags(&side.s, hipStreamNonBlocking)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&side.fork, hipEventDisableTiming)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&side.join, hipEventDisableTiming)) != hipSuccess) return e;
+  if (!side.ready) {
+    // default priority (the only one used anywhere in this library); a
+    // failed creation leaves nothing behind and is retried by the next call
+    if (side.s == nullptr && (e = hipStreamCreateWithFlags(&side.s, hipStreamNonBlocking)) != hipSuccess) {
+      side.s = nullptr;
+      return e;
+    }
+    if (side.fork == nullptr && (e = hipEventCreateWithFlags(&side.fork, hipEventDisableTiming)) != hipSuccess) {
+      side.fork = nullptr;
+      return e;
+    }
+    if (side.join == nullptr && (e = hipEventCreateWithFlags(&side.join, hipEventDisableTiming)) != hipSuccess) {
+      side.join = nullptr;
+      return e;
+    }
+    side.ready = true;
   }
   if ((e = hipEventRecord(side.fork, st)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(side.s, side.fork, 0)) != hipSuccess) return e;
