@@ -34,12 +34,14 @@ def _qkv_dev(B, Hq, Hkv, n, d, dtype, seed, gpu, scale_q=1.0):
 
 # ------------------------------------------------------------------ bins --
 
-def _expected_plan(delta, u, n):
+def _expected_plan(delta, u, n, tiles=None):
+    """Block starts and the plan records of `tiles` (all tiles if None; the
+    other rows of the returned array are left zero)."""
     st = oracle.block_starts(delta, u, n)
     ntile = (n + 127) // 128
     rec = np.zeros((ntile, 8), dtype=np.int64)
     starts_set = set(st.tolist()) | {n}
-    for q in range(ntile):
+    for q in (range(ntile) if tiles is None else tiles):
         r0 = 128 * q
         rl = min(r0 + 127, n - 1)
         a, e = oracle.block_of(delta, u, n, [r0, rl])
@@ -52,20 +54,23 @@ def _expected_plan(delta, u, n):
     return st, rec
 
 
-def _check_bins(bins, delta, u, n):
+def _check_bins(bins, delta, u, n, tiles=None):
+    """Block counts and starts of every hash, and the plan records of `tiles`
+    (every tile if None), bit-exact against the oracle."""
     nblk = bins.nblk.cpu().numpy()
     starts = bins.starts.cpu().numpy()
     plan = bins.plan.cpu().numpy().view(np.uint32).astype(np.int64)
     H, s = delta.shape
+    sel = slice(None) if tiles is None else np.asarray(tiles)
     for h in range(H):
         for i in range(s):
             t = h * s + i
-            st, rec = _expected_plan(delta[h, i], u[h, i], n)
+            st, rec = _expected_plan(delta[h, i], u[h, i], n, tiles)
             assert nblk[t] == st.size, (h, i, delta[h, i], u[h, i], n)
             assert np.array_equal(starts[t, :st.size + 1], np.append(st, n)), (h, i, delta[h, i], u[h, i], n)
             got = plan[h, :, i, :].copy()
             got[:, :4] = plan[h, :, i, :4].astype(np.uint32).view(np.int32)
-            assert np.array_equal(got, rec), (h, i, delta[h, i], u[h, i], n)
+            assert np.array_equal(got[sel], rec[sel]), (h, i, delta[h, i], u[h, i], n)
 
 
 @pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 127, 128, 129, 1000, 4097])
@@ -203,6 +208,39 @@ def test_workload_full_size_sampled_rows(gpu, name):
         got = to64(o[0, h, torch.as_tensor(rows, device=gpu)])
         worst = max(worst, check_slices(got[None], ref[None], W.dtype, where=f"{name} head {h}"))
     say(f"  worst rel err {worst:.3e}")
+
+
+def test_maximum_length(gpu):
+    """n at the library's maximum (PLPSH_MAX_N): the bin kernel's word array
+    is then at its largest (about 128 KB of LDS per hash), checked bit-exact
+    for edge and wide widths, and a causal attention over the whole length is
+    checked on sampled rows (first and last rows, tile edges, random rows)."""
+    n = P._binding.MAX_N
+    say(f"maximum length n={n}: bins")
+    delta = np.array([[0.7, 2.5, 37.0, 5000.25]])
+    u = np.array([[0.3, 0.0, 36.9, 1234.5]])
+    bins = P.bins_from_hashes(delta, u, n, device=gpu)
+    torch.cuda.synchronize()
+    ntile = (n + 127) // 128
+    tiles = sorted({0, 1, 2, ntile - 2, ntile - 1} | set(np.random.default_rng(3).choice(ntile, 40, replace=False).tolist()))
+    _check_bins(bins, delta, u, n, tiles)
+    say(f"maximum length n={n}: attention")
+    B, Hq, Hkv, d, s = 1, 2, 1, 64, 6
+    sig = (3.0, 120.0)
+    q, k, v = synth.qkv_torch(B, Hq, Hkv, n, d, "bf16", 4242, gpu)
+    o = torch.full_like(q, float("nan"))
+    P.attention(q, k, v, sig, s, seed=11, causal=True, out=o)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any().item(), "output not fully written"
+    od, ou = oracle.sample_hashes(11, sig, s)
+    rng = np.random.default_rng(8)
+    kh, vh = to64(k[0, 0]), to64(v[0, 0])
+    for h in range(Hq):
+        rows = sample_rows(n, 12, rng)
+        qh = to64(q[0, h, torch.as_tensor(rows, device=gpu)])
+        ref = oracle.plsh_attention_rows(qh, kh, vh, od[h], ou[h], rows, True)
+        got = to64(o[0, h, torch.as_tensor(rows, device=gpu)])
+        check_slices(got[None], ref[None], "bf16", where=f"n={n} head {h}")
 
 
 def test_one_block_is_plain_attention(gpu):
