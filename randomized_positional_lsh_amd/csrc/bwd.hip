@@ -736,12 +736,16 @@ hipError_t launch_plsh_bwd(const void* q, const void* k, const void* v, const vo
   }
   if ((e = hipEventRecord(side.fork, st)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(side.s, side.fork, 0)) != hipSuccess) return e;
-  e = launch_bwd_dir<true>(a, okv, d, causal, 8 * a.cs * batch * hkv, side.s);
-  if (e != hipSuccess) return e;
-  if ((e = hipEventRecord(side.join, side.s)) != hipSuccess) return e;
-  e = launch_bwd_dir<false>(a, oq, d, causal, 8 * a.cs * batch * hq, st);
-  if (e != hipSuccess) return e;
-  return hipStreamWaitEvent(st, side.join, 0);
+  // once forked, the caller's stream always waits for the second stream,
+  // also when a launch fails, so that nothing on it outlives the call's order
+  const hipError_t ekv = launch_bwd_dir<true>(a, okv, d, causal, 8 * a.cs * batch * hkv, side.s);
+  const hipError_t ej = hipEventRecord(side.join, side.s);
+  const hipError_t eq = ekv == hipSuccess ? launch_bwd_dir<false>(a, oq, d, causal, 8 * a.cs * batch * hq, st)
+                                          : hipSuccess;
+  const hipError_t ew = ej == hipSuccess ? hipStreamWaitEvent(st, side.join, 0) : ej;
+  if (ekv != hipSuccess) return ekv;
+  if (eq != hipSuccess) return eq;
+  return ew;
 }
 
 }  // namespace plpsh
