@@ -708,7 +708,7 @@ hipError_t launch_plsh_bwd(const void* q, const void* k, const void* v, const vo
   BwdOrder oq{}, okv{};
   for (int i = 0; i < hq; ++i) oq.w[i >> 1] |= static_cast<uint32_t>(head_order[i]) << (16 * (i & 1));
   for (int i = 0; i < hkv; ++i) okv.w[i >> 1] |= static_cast<uint32_t>(kv_order[i]) << (16 * (i & 1));
-  // dK/dV on a second stream of the device, beside dQ on the caller's stream
+  // dK/dV and dQ on two streams of the device, the caller's and a second one
   // (both read the same inputs and D, and write different outputs), so that
   // each kernel fills the other's tail; joined back to the caller's stream.
   int dev = 0;
@@ -736,15 +736,25 @@ hipError_t launch_plsh_bwd(const void* q, const void* k, const void* v, const vo
   }
   if ((e = hipEventRecord(side.fork, st)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(side.s, side.fork, 0)) != hipSuccess) return e;
-  // once forked, the caller's stream always waits for the second stream,
-  // also when a launch fails, so that nothing on it outlives the call's order
-  const hipError_t ekv = launch_bwd_dir<true>(a, okv, d, causal, 8 * a.cs * batch * hkv, side.s);
+  // Which kernel goes to the second stream: a dK/dV work item covers the
+  // keys of all hq / hkv query heads of its group, so with four or more per
+  // group its work items are the heavier ones and go there, otherwise the dQ
+  // kernel does (interleaved timing: the Mistral layer, 4 per group, 614
+  // against 624 us; the Qwen3 layer, 2 per group, 195 against 224 us; 8
+  // heads without groups, 72 against 79 us).  Once forked, the caller's
+  // stream always waits for the second stream, also when a launch fails, so
+  // that nothing on it outlives the call's order.
+  const bool kv_side = hq >= 4 * hkv;
+  const int gq = 8 * a.cs * batch * hq, gkv = 8 * a.cs * batch * hkv;
+  const hipError_t e1 = kv_side ? launch_bwd_dir<true>(a, okv, d, causal, gkv, side.s)
+                                : launch_bwd_dir<false>(a, oq, d, causal, gq, side.s);
   const hipError_t ej = hipEventRecord(side.join, side.s);
-  const hipError_t eq = ekv == hipSuccess ? launch_bwd_dir<false>(a, oq, d, causal, 8 * a.cs * batch * hq, st)
-                                          : hipSuccess;
+  const hipError_t e2 = e1 != hipSuccess ? hipSuccess
+                        : kv_side        ? launch_bwd_dir<false>(a, oq, d, causal, gq, st)
+                                         : launch_bwd_dir<true>(a, okv, d, causal, gkv, st);
   const hipError_t ew = ej == hipSuccess ? hipStreamWaitEvent(st, side.join, 0) : ej;
-  if (ekv != hipSuccess) return ekv;
-  if (eq != hipSuccess) return eq;
+  if (e1 != hipSuccess) return e1;
+  if (e2 != hipSuccess) return e2;
   return ew;
 }
 

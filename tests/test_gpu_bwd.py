@@ -153,15 +153,17 @@ def test_gradients_full_size(gpu):
     assert (dk_sum.abs() <= 2e-2 * dk_scale + 1e-6).all().item()
 
 
-def test_gradients_ordered_on_the_callers_stream(gpu):
-    """The dK/dV kernel runs on a second stream of the device, forked from and
-    joined back to the caller's stream: copies enqueued on the caller's
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 4)], ids=["dKdV-on-second-stream", "dQ-on-second-stream"])
+def test_gradients_ordered_on_the_callers_stream(gpu, Hq, Hkv):
+    """One of the two backward kernels runs on a second stream of the device
+    (dK/dV with four or more query heads per KV head, else dQ), forked from
+    and joined back to the caller's stream: copies enqueued on the caller's
     (non-default) stream right after the call, with no device-wide
     synchronisation, must see every gradient, bit-identical to a call on the
     default stream.  The outputs are filled with NaN before each call."""
-    B, Hq, Hkv, n, d, s = 1, 8, 2, 2048, 128, 20
+    B, n, d, s = 1, 2048, 128, 20
     sig = synth.alibi_sigmas(Hq)
-    say("backward ordering on a side stream")
+    say(f"backward ordering on a side stream, Hq={Hq} Hkv={Hkv}")
     (q, k, v, do), _ = _dev(B, Hq, Hkv, n, d, 91, gpu)
     ldelta, lu, bins = P.sample_bins(3, sig, s, n, device=gpu)
     o, lse = P.attention_lse(q, k, v, bins, causal=True, delta=ldelta)
