@@ -14,7 +14,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libplpsh.so")
+# PLPSH_LIBRARY names another build of the same library (the host-sanitizer
+# build of sanitize.py); by default the in-tree libplpsh.so is loaded
+LIB_PATH = os.environ.get("PLPSH_LIBRARY") or os.path.join(_HERE, "libplpsh.so")
 
 OK = 0
 INVALID_ARGUMENT = 1
@@ -142,11 +144,45 @@ def workspace_bytes(heads_q: int, s: int, n: int) -> int:
     return int(_lib.plpsh_workspace_bytes(heads_q, s, n))
 
 
-def _stream(stream):
+def _torch_stream(stream):
     import torch
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+    return torch.cuda.current_stream() if stream is None else stream
+
+
+def _stream(stream):
+    return ctypes.c_void_p(_torch_stream(stream).cuda_stream)
+
+
+def _on_stream(stream):
+    """Context in which tensors are allocated for work enqueued on `stream`:
+    the caching allocator then hands their memory to other work only in that
+    stream's order, never while the library's kernels may still use it."""
+    import torch
+    return torch.cuda.stream(_torch_stream(stream))
+
+
+def _check_like(t, like, name, dtype=None, shape=None):
+    """A caller-supplied output or gradient must match what the kernels write:
+    the shape, dtype and device of `like` (or those given), contiguous."""
+    want_shape = tuple(like.shape) if shape is None else tuple(shape)
+    want_dtype = like.dtype if dtype is None else dtype
+    if tuple(t.shape) != want_shape:
+        raise ValueError(f"{name} must have shape {want_shape}, not {tuple(t.shape)}")
+    if t.dtype != want_dtype:
+        raise ValueError(f"{name} must be {want_dtype}, not {t.dtype}")
+    if t.device != like.device:
+        raise ValueError(f"{name} must be on {like.device}, not {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _out_like(out, like, name="out", stream=None):
+    import torch
+    if out is None:
+        with _on_stream(stream):
+            return torch.empty_like(like)
+    return _check_like(out, like, name)
 
 
 def _torch_dtype_code(t) -> int:
@@ -173,10 +209,11 @@ class Bins:
         self.plan = b8[L["plan"]:L["plan"] + 32 * heads * ntile * s].view(torch.int32).view(heads, ntile, s, 8)
 
 
-def _bins_buffer(heads, s, n, device):
+def _bins_buffer(heads, s, n, device, stream=None):
     import torch
     nbytes = bins_layout(heads, s, n)["total"]
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    with _on_stream(stream):
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
 def sample_bins(seed: int, sigma, s: int, n: int, device="cuda", stream=None, buffer=None, delta=None, u=None):
@@ -188,7 +225,7 @@ def sample_bins(seed: int, sigma, s: int, n: int, device="cuda", stream=None, bu
     H = sig.size
     delta = np.empty((H, s)) if delta is None else delta
     u = np.empty((H, s)) if u is None else u
-    buf = _bins_buffer(H, s, n, device) if buffer is None else buffer
+    buf = _bins_buffer(H, s, n, device, stream) if buffer is None else buffer
     _check(_lib.plpsh_sample_bins(ctypes.c_uint64(seed & (2 ** 64 - 1)), H, s, n, _ptr(sig), _ptr(delta), _ptr(u),
                                   ctypes.c_void_p(buf.data_ptr()), buf.numel(), _stream(stream)),
            "plpsh_sample_bins")
@@ -199,7 +236,7 @@ def bins_from_hashes(delta, u, n: int, device="cuda", stream=None) -> Bins:
     d = _f64(delta)
     uu = _f64(u)
     H, s = d.shape
-    buf = _bins_buffer(H, s, n, device)
+    buf = _bins_buffer(H, s, n, device, stream)
     _check(_lib.plpsh_bins_from_hashes(H, s, n, _ptr(d), _ptr(uu), ctypes.c_void_p(buf.data_ptr()), buf.numel(),
                                        _stream(stream)), "plpsh_bins_from_hashes")
     return Bins(buf, H, s, n)
@@ -218,11 +255,14 @@ def _qkv_shapes(q, k, v):
     return B, Hq, k.shape[1], n, d
 
 
-def _workspace(workspace, heads_q, s, n, device):
+def _workspace(workspace, heads_q, s, n, device, stream=None):
     import torch
     need = workspace_bytes(heads_q, s, n)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        with _on_stream(stream):
+            workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    elif workspace.device != device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
     return workspace
 
 
@@ -234,8 +274,8 @@ def attention(q, k, v, sigma, s: int, seed: int = 0, causal: bool = False, out=N
     sig = _f64(sigma).reshape(-1)
     if sig.size != Hq:
         raise ValueError("sigma must have one entry per query head")
-    out = torch.empty_like(q) if out is None else out
-    ws = _workspace(workspace, Hq, s, n, q.device)
+    out = _out_like(out, q, stream=stream)
+    ws = _workspace(workspace, Hq, s, n, q.device, stream)
     st = _lib.plpsh_attention_fwd(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
                                   ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()), B, Hq, Hkv, n, d,
                                   _torch_dtype_code(q), _ptr(sig), s, ctypes.c_uint64(seed & (2 ** 64 - 1)),
@@ -253,8 +293,8 @@ def attention_hashes(q, k, v, delta, u, causal: bool = False, out=None, workspac
     if dl.ndim != 2 or dl.shape[0] != Hq or uu.shape != dl.shape:
         raise ValueError("delta and u must be [heads_q, s]")
     s = dl.shape[1]
-    out = torch.empty_like(q) if out is None else out
-    ws = _workspace(workspace, Hq, s, n, q.device)
+    out = _out_like(out, q, stream=stream)
+    ws = _workspace(workspace, Hq, s, n, q.device, stream)
     st = _lib.plpsh_attention_fwd_hashes(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
                                          ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()), B, Hq, Hkv,
                                          n, d, _torch_dtype_code(q), _ptr(dl), _ptr(uu), s, int(bool(causal)),
@@ -270,8 +310,8 @@ def fixed_blocks(q, k, v, block, causal: bool = False, out=None, workspace=None,
     import torch
     B, Hq, Hkv, n, d = _qkv_shapes(q, k, v)
     bl = np.ascontiguousarray(np.broadcast_to(np.asarray(block, dtype=np.int32), (Hq,)))
-    out = torch.empty_like(q) if out is None else out
-    ws = _workspace(workspace, Hq, 1, n, q.device)
+    out = _out_like(out, q, stream=stream)
+    ws = _workspace(workspace, Hq, 1, n, q.device, stream)
     st = _lib.plpsh_fixed_blocks_fwd(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
                                      ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()), B, Hq, Hkv, n, d,
                                      _torch_dtype_code(q), bl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
@@ -286,7 +326,7 @@ def _on_bins(fn, name, q, k, v, bins, causal, delta, out, stream):
     if bins.heads != Hq or bins.n != n:
         raise ValueError("bins were computed for other sizes")
     dl = None if delta is None else _f64(delta)
-    out = torch.empty_like(q) if out is None else out
+    out = _out_like(out, q, stream=stream)
     st = fn(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
             ctypes.c_void_p(out.data_ptr()), B, Hq, Hkv, n, d, _torch_dtype_code(q), bins.s, int(bool(causal)),
             ctypes.c_void_p(bins.buffer.data_ptr()), bins.buffer.numel(), None if dl is None else _ptr(dl),
@@ -316,8 +356,14 @@ def attention_lse(q, k, v, bins: "Bins", causal: bool = False, delta=None, out=N
     if bins.heads != Hq or bins.n != n:
         raise ValueError("bins were computed for other sizes")
     dl = None if delta is None else _f64(delta)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device) if lse is None else lse
+    if lse is not None:
+        _check_like(lse, q, "lse", dtype=torch.float32, shape=(B, Hq, n))
+    out = _out_like(out, q, stream=stream)
+    if lse is None:
+        with _on_stream(stream):
+            lse = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device)
+    else:
+        _check_like(lse, q, "lse", dtype=torch.float32, shape=(B, Hq, n))
     st = _lib.plpsh_attention_fwd_lse(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
                                       ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()),
                                       ctypes.c_void_p(lse.data_ptr()), B, Hq, Hkv, n, d, _torch_dtype_code(q), bins.s,
@@ -335,11 +381,23 @@ def attention_bwd(q, k, v, out, dout, lse, bins: "Bins", causal: bool = False, d
     if bins.heads != Hq or bins.n != n:
         raise ValueError("bins were computed for other sizes")
     dl = None if delta is None else _f64(delta)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    _check_like(out, q, "out")
+    _check_like(dout, q, "dout")
+    _check_like(lse, q, "lse", dtype=torch.float32, shape=(B, Hq, n))
+    for t, like, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        if t is not None:
+            _check_like(t, like, name)
+    dq = _out_like(dq, q, "dq", stream)
+    dk = _out_like(dk, k, "dk", stream)
+    dv = _out_like(dv, v, "dv", stream)
     need = int(_lib.plpsh_attention_bwd_workspace_bytes(B, Hq, n))
-    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    if workspace is None:
+        with _on_stream(stream):
+            ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    else:
+        ws = workspace
+        if ws.device != q.device or not ws.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the inputs' device")
     ptr = lambda t: ctypes.c_void_p(t.data_ptr())
     st = _lib.plpsh_attention_bwd(ptr(q), ptr(k), ptr(v), ptr(out), ptr(dout), ptr(lse), ptr(dq), ptr(dk), ptr(dv),
                                   B, Hq, Hkv, n, d, _torch_dtype_code(q), bins.s, int(bool(causal)),
@@ -356,7 +414,7 @@ def alibi_dense(q, k, v, sigma, causal: bool = False, out=None, stream=None):
     sig = _f64(sigma).reshape(-1)
     if sig.size != Hq:
         raise ValueError("sigma must have one entry per query head")
-    out = torch.empty_like(q) if out is None else out
+    out = _out_like(out, q, stream=stream)
     st = _lib.plpsh_alibi_dense_fwd(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
                                     ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()), B, Hq, Hkv, n, d,
                                     _torch_dtype_code(q), _ptr(sig), int(bool(causal)), _stream(stream))
@@ -376,7 +434,11 @@ def error_rowmax(sigma: float, bins: "Bins", out=None, stream=None):
     import torch
     if bins.heads != 1:
         raise ValueError("error functions take the bins of one head")
-    out = torch.empty(bins.n, dtype=torch.float64, device=bins.buffer.device) if out is None else out
+    if out is None:
+        with _on_stream(stream):
+            out = torch.empty(bins.n, dtype=torch.float64, device=bins.buffer.device)
+    else:
+        _check_like(out, bins.buffer, "out", dtype=torch.float64, shape=(bins.n,))
     _check(_lib.plpsh_error_rowmax(float(sigma), bins.n, bins.s, ctypes.c_void_p(bins.buffer.data_ptr()),
                                    bins.buffer.numel(), ctypes.c_void_p(out.data_ptr()), _stream(stream)),
            "plpsh_error_rowmax")
@@ -390,9 +452,13 @@ def error_matvec(sigma: float, bins: "Bins", x, out=None, workspace=None, stream
         raise ValueError("error functions take the bins of one head")
     if x.dtype != torch.float64 or x.numel() != bins.n or not x.is_contiguous():
         raise ValueError("x must be a contiguous float64 vector of length n")
-    out = torch.empty_like(x) if out is None else out
+    out = _out_like(out, x, stream=stream)
     need = error_workspace_bytes(bins.n, bins.s, 0)
-    ws = torch.empty(need, dtype=torch.uint8, device=x.device) if workspace is None else workspace
+    if workspace is None:
+        with _on_stream(stream):
+            ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    else:
+        ws = workspace
     _check(_lib.plpsh_error_matvec(float(sigma), bins.n, bins.s, ctypes.c_void_p(bins.buffer.data_ptr()),
                                    bins.buffer.numel(), ctypes.c_void_p(x.data_ptr()),
                                    ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
@@ -411,7 +477,11 @@ def error_norms(sigma: float, delta, u, n: int, max_steps: int = 300, tol: float
     need = error_workspace_bytes(n, s, max_steps)
     if need == 0:
         raise ValueError("invalid sizes")
-    ws = torch.empty(need, dtype=torch.uint8, device=device) if workspace is None else workspace
+    if workspace is None:
+        with _on_stream(stream):
+            ws = torch.empty(need, dtype=torch.uint8, device=device)
+    else:
+        ws = workspace
     spec = ctypes.c_double()
     mx = ctypes.c_double()
     row = ctypes.c_int32()

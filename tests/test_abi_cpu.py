@@ -235,3 +235,43 @@ def test_empty_calls_are_noops():
     lib = B.raw()
     sig = np.array([1.0, 2.0])
     assert lib.plpsh_alibi_dense_fwd(FAKE, FAKE, FAKE, FAKE, 0, 2, 1, 64, 64, 1, B._ptr(sig), 0, None) == 0
+
+
+def test_binding_checks_caller_outputs_before_the_c_abi():
+    """The Python wrappers reject an output or gradient tensor whose shape,
+    dtype or layout differs from what the kernels write (an fp32 input with
+    a bf16 output would otherwise be written past its end), before any call
+    into the library."""
+    import torch
+    q = torch.zeros((1, 2, 64, 64), dtype=torch.float32)
+    k = torch.zeros((1, 1, 64, 64), dtype=torch.float32)
+    bad_outs = [torch.zeros((1, 2, 64, 64), dtype=torch.bfloat16),       # dtype
+                torch.zeros((1, 2, 63, 64), dtype=torch.float32),        # shape
+                torch.zeros((1, 2, 64, 128), dtype=torch.float32)[..., ::2]]  # not contiguous
+    for out in bad_outs:
+        with pytest.raises(ValueError):
+            P.attention(q, k, k, [2.0, 3.0], 4, out=out)
+        with pytest.raises(ValueError):
+            P.alibi_dense(q, k, k, [2.0, 3.0], out=out)
+        with pytest.raises(ValueError):
+            P.attention_hashes(q, k, k, np.full((2, 4), 3.0), np.zeros((2, 4)), out=out)
+    qb, kb = q.bfloat16(), k.bfloat16()
+    lse = torch.zeros((1, 2, 64), dtype=torch.float32)
+    bins = type("FakeBins", (), {"heads": 2, "n": 64, "s": 4})()
+    # backward: out, dout and lse are read; dq, dk, dv are written
+    with pytest.raises(ValueError):
+        P.attention_bwd(qb, kb, kb, qb[:, :, :32], qb, lse, bins)
+    with pytest.raises(ValueError):
+        P.attention_bwd(qb, kb, kb, qb, qb.float(), lse, bins)
+    with pytest.raises(ValueError):
+        P.attention_bwd(qb, kb, kb, qb, qb, lse.double(), bins)
+    with pytest.raises(ValueError):
+        P.attention_bwd(qb, kb, kb, qb, qb, lse[:, :1], bins)
+    with pytest.raises(ValueError):
+        P.attention_bwd(qb, kb, kb, qb, qb, lse, bins, dq=torch.zeros_like(kb))
+    with pytest.raises(ValueError):
+        P.attention_bwd(qb, kb, kb, qb, qb, lse, bins, dk=torch.zeros_like(qb))
+    with pytest.raises(ValueError):
+        P.attention_bwd(qb, kb, kb, qb, qb, lse, bins, dv=torch.zeros_like(kb).float())
+    with pytest.raises(ValueError):
+        P.attention_lse(qb, kb, kb, bins, lse=lse[:, :, :10])
