@@ -1054,13 +1054,8 @@ template <int D, bool BF, bool CAUSAL, int NCH, int MODE>
 hipError_t launch_one(const FwdArgs& a, const HeadOrder& ord, const HeadScale& hs, int grid, hipStream_t st) {
   constexpr int lds = Geo<D, BF>::BIG + SMALL;
   auto kfn = fwd_kernel<D, BF, CAUSAL, NCH, MODE>;
-  static bool attr_done = false;  // benign race: idempotent
-  if (lds > 64 * 1024 && !attr_done) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  static LdsOptIn opt;
+  if (hipError_t e = opt.ensure(reinterpret_cast<const void*>(kfn), lds); e != hipSuccess) return e;
   hipLaunchKernelGGL(kfn, dim3(grid), dim3(NT), lds, st, a, ord, hs);
   return hipGetLastError();
 }

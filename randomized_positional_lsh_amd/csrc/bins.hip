@@ -245,13 +245,8 @@ hipError_t launch_bins(const double* du, int heads, int s, int n, void* bins, hi
   const int nwords = 4 * ntile + 4;  // covers positions < 128 (ntile + 1)
   const size_t lds = static_cast<size_t>(nwords) * 2 * sizeof(uint32_t);
   // opt in to the dynamic LDS this launch needs (the largest request so far)
-  static size_t attr_bytes = 0;  // benign race: the attribute only grows
-  if (lds > 64 * 1024 && lds > attr_bytes) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bins_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    attr_bytes = lds;
-  }
+  static LdsOptIn opt;
+  if (hipError_t e = opt.ensure(reinterpret_cast<const void*>(&bins_kernel), lds); e != hipSuccess) return e;
   hipLaunchKernelGGL(bins_kernel, dim3(heads * s), dim3(kThreads), lds, stream, du, n, s, ntile, nwords,
                      reinterpret_cast<int32_t*>(base + L.off_nblk),
                      reinterpret_cast<int32_t*>(base + L.off_starts),

@@ -644,13 +644,8 @@ template <int D, bool CAUSAL, int NCH, bool KEYSIDE>
 hipError_t launch_bwd_one(const BwdArgs& a, const BwdOrder& ord, int grid, hipStream_t st) {
   constexpr int lds = BG<D>::BIG + SMALL;
   auto kfn = bwd_kernel<D, CAUSAL, NCH, KEYSIDE>;
-  static bool attr = false;  // benign race: idempotent
-  if (lds > 64 * 1024 && !attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       lds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static LdsOptIn opt;
+  if (hipError_t e = opt.ensure(reinterpret_cast<const void*>(kfn), lds); e != hipSuccess) return e;
   hipLaunchKernelGGL(kfn, dim3(grid), dim3(NT), lds, st, a, ord);
   return hipGetLastError();
 }

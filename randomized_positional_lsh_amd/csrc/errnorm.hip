@@ -296,15 +296,8 @@ size_t err_dots_bytes(int m) { return static_cast<size_t>(m) * kDotSplit * sizeo
 
 hipError_t launch_err_rowmax(const PlanRec* plan, int n, int s, double sigma, double* rowmax, hipStream_t st) {
   const size_t lds = 2 * static_cast<size_t>(s) * kRowsPerBlock * sizeof(int);
-  if (lds > 64 * 1024) {
-    static bool attr = false;  // benign race: idempotent
-    if (!attr) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(rowmax_kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-      if (e != hipSuccess) return e;
-      attr = true;
-    }
-  }
+  static LdsOptIn opt;
+  if (hipError_t e = opt.ensure(reinterpret_cast<const void*>(rowmax_kernel), lds); e != hipSuccess) return e;
   hipLaunchKernelGGL(rowmax_kernel, dim3(cdiv(n, kRowsPerBlock)), dim3(kRowsPerBlock), lds, st, plan, n, s, sigma,
                      rowmax);
   return hipGetLastError();

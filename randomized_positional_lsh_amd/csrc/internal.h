@@ -1,8 +1,11 @@
 // Internal declarations shared by the host API and the kernel launchers.
 #pragma once
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 
 namespace plpsh {
 
@@ -16,6 +19,31 @@ struct alignas(16) PlanRec {
 static_assert(sizeof(PlanRec) == 32, "plan record is 32 bytes");
 
 constexpr int kPlanTile = 128;
+
+// Dynamic LDS above the 64 KB default needs an opt-in per kernel, and
+// hipFuncSetAttribute applies to the device current at the call.  One
+// LdsOptIn per kernel records, per device, the largest size granted there, so
+// every device is opted in on its first launch and again whenever a launch
+// needs more.
+constexpr int kMaxDevices = 64;
+struct LdsOptIn {
+  std::atomic<size_t> granted[kMaxDevices] = {};
+  std::mutex mu;
+  hipError_t ensure(const void* fn, size_t need) {
+    if (need <= 64 * 1024) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    if (granted[dev].load(std::memory_order_acquire) >= need) return hipSuccess;
+    std::lock_guard<std::mutex> lock(mu);
+    if (granted[dev].load(std::memory_order_relaxed) >= need) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(need));
+    if (e != hipSuccess) return e;
+    granted[dev].store(need, std::memory_order_release);
+    return hipSuccess;
+  }
+};
 
 struct BinsLayout {
   size_t off_nblk, off_starts, off_plan, total;
