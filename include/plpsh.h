@@ -60,6 +60,9 @@ typedef enum {
     PLPSH_ERR_HIP = 4                 /* HIP runtime / launch error */
 } plpsh_status;
 
+/* Element types.  Entry points take the type as an int32_t `dtype` holding
+ * one of these values (any other value is rejected with
+ * PLPSH_ERR_INVALID_ARGUMENT). */
 typedef enum {
     PLPSH_DTYPE_F32 = 0,    /* float32 Q/K/V/O; fp32 matrix cores, fp32 softmax */
     PLPSH_DTYPE_BF16 = 1    /* bfloat16 Q/K/V/O; bf16 matrix cores, fp32 accumulation */
@@ -71,8 +74,10 @@ typedef enum {
 #define PLPSH_MAX_HASHES 65536     /* heads * s per call */
 #define PLPSH_PLAN_TILE 128        /* query rows per plan record */
 
-/* Human-readable name of a status code (static storage). */
-const char* plpsh_status_string(plpsh_status st);
+/* Human-readable name of a status code (static storage).  Takes the code as
+ * a plain integer so that any value is accepted: codes outside plpsh_status
+ * give "PLPSH_ERR_UNKNOWN". */
+const char* plpsh_status_string(int32_t status);
 
 /* Library version string (static storage). */
 const char* plpsh_version(void);
@@ -188,7 +193,7 @@ size_t plpsh_workspace_bytes(int32_t heads_q, int32_t s, int32_t n);
  */
 plpsh_status plpsh_attention_fwd(const void* q, const void* k, const void* v, void* o,
                                  int32_t batch, int32_t heads_q, int32_t heads_kv,
-                                 int32_t n, int32_t head_dim, plpsh_dtype dtype,
+                                 int32_t n, int32_t head_dim, int32_t dtype,
                                  const double* sigma, int32_t s, uint64_t seed,
                                  int32_t causal, void* workspace, size_t workspace_bytes,
                                  void* stream);
@@ -202,7 +207,7 @@ plpsh_status plpsh_attention_fwd(const void* q, const void* k, const void* v, vo
  */
 plpsh_status plpsh_attention_fwd_hashes(const void* q, const void* k, const void* v, void* o,
                                         int32_t batch, int32_t heads_q, int32_t heads_kv,
-                                        int32_t n, int32_t head_dim, plpsh_dtype dtype,
+                                        int32_t n, int32_t head_dim, int32_t dtype,
                                         const double* delta, const double* u, int32_t s,
                                         int32_t causal, void* workspace, size_t workspace_bytes,
                                         void* stream);
@@ -222,7 +227,7 @@ plpsh_status plpsh_attention_fwd_hashes(const void* q, const void* k, const void
  */
 plpsh_status plpsh_fixed_blocks_fwd(const void* q, const void* k, const void* v, void* o,
                                     int32_t batch, int32_t heads_q, int32_t heads_kv,
-                                    int32_t n, int32_t head_dim, plpsh_dtype dtype,
+                                    int32_t n, int32_t head_dim, int32_t dtype,
                                     const int32_t* block, int32_t causal,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
@@ -241,7 +246,7 @@ plpsh_status plpsh_fixed_blocks_fwd(const void* q, const void* k, const void* v,
  */
 plpsh_status plpsh_attention_fwd_bins(const void* q, const void* k, const void* v, void* o,
                                       int32_t batch, int32_t heads_q, int32_t heads_kv,
-                                      int32_t n, int32_t head_dim, plpsh_dtype dtype,
+                                      int32_t n, int32_t head_dim, int32_t dtype,
                                       int32_t s, int32_t causal, const void* bins,
                                       size_t bins_bytes, const double* delta, void* stream);
 
@@ -259,7 +264,7 @@ plpsh_status plpsh_attention_fwd_bins(const void* q, const void* k, const void* 
  */
 plpsh_status plpsh_attention_fwd_literal(const void* q, const void* k, const void* v, void* o,
                                          int32_t batch, int32_t heads_q, int32_t heads_kv,
-                                         int32_t n, int32_t head_dim, plpsh_dtype dtype,
+                                         int32_t n, int32_t head_dim, int32_t dtype,
                                          int32_t s, int32_t causal, const void* bins,
                                          size_t bins_bytes, const double* delta, void* stream);
 
@@ -273,7 +278,7 @@ plpsh_status plpsh_attention_fwd_literal(const void* q, const void* k, const voi
  */
 plpsh_status plpsh_attention_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse,
                                      int32_t batch, int32_t heads_q, int32_t heads_kv,
-                                     int32_t n, int32_t head_dim, plpsh_dtype dtype,
+                                     int32_t n, int32_t head_dim, int32_t dtype,
                                      int32_t s, int32_t causal, const void* bins,
                                      size_t bins_bytes, const double* delta, void* stream);
 
@@ -299,16 +304,19 @@ size_t plpsh_attention_bwd_workspace_bytes(int32_t batch, int32_t heads_q, int32
  *                plpsh_attention_bwd_workspace_bytes(batch, heads_q, n).
  * bf16 only (PLPSH_ERR_UNSUPPORTED for f32); head_dim 64 or 128.  Arithmetic:
  * bf16 products on the matrix cores with fp32 accumulation; P and dS are
- * rounded to bf16 before their products.  Asynchronous on `stream`: the dK/dV
- * kernel runs on a second stream of the device (created on first use, default
- * priority, kept until the process ends) beside the dQ kernel, forked from and
- * joined back to `stream` with events, so work issued to `stream` afterwards
- * sees all three gradients.  Calls from several threads are serialised around
- * that fork and join.
+ * rounded to bf16 before their products.  Asynchronous on `stream`: the dQ
+ * kernel and the dK/dV kernel run side by side on two streams of the device,
+ * `stream` and a second one (created on first use, default priority, kept
+ * until the process ends), forked from and joined back to `stream` with
+ * events, so work issued to `stream` afterwards sees all three gradients.
+ * The second stream takes the kernel with the heavier work items: dK/dV
+ * (whose work items cover every query head of a KV group) when heads_q >=
+ * 4 * heads_kv, dQ otherwise.  Calls from several threads are serialised
+ * around that fork and join.
  */
 plpsh_status plpsh_attention_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                                  const float* lse, void* dq, void* dk, void* dv, int32_t batch, int32_t heads_q,
-                                 int32_t heads_kv, int32_t n, int32_t head_dim, plpsh_dtype dtype, int32_t s,
+                                 int32_t heads_kv, int32_t n, int32_t head_dim, int32_t dtype, int32_t s,
                                  int32_t causal, const void* bins, size_t bins_bytes, const double* delta,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
@@ -322,7 +330,7 @@ plpsh_status plpsh_attention_bwd(const void* q, const void* k, const void* v, co
  */
 plpsh_status plpsh_alibi_dense_fwd(const void* q, const void* k, const void* v, void* o,
                                    int32_t batch, int32_t heads_q, int32_t heads_kv,
-                                   int32_t n, int32_t head_dim, plpsh_dtype dtype,
+                                   int32_t n, int32_t head_dim, int32_t dtype,
                                    const double* sigma, int32_t causal, void* stream);
 
 /* ------------------------------------------------------------------------

@@ -25,7 +25,7 @@ bool hip_failed(hipError_t e, const char* what) {
   return true;
 }
 
-constexpr int kMaxDevices = 64;
+using plpsh::kMaxDevices;
 constexpr int kSlots = 8;
 constexpr size_t kSlotBytes = static_cast<size_t>(PLPSH_MAX_HASHES) * 2 * sizeof(double);
 
@@ -247,7 +247,7 @@ const plpsh::PlanRec* plan_of(const void* bins, int s, int n) {
 
 extern "C" {
 
-const char* plpsh_status_string(plpsh_status st) {
+const char* plpsh_status_string(int32_t st) {
   switch (st) {
     case PLPSH_OK: return "PLPSH_OK";
     case PLPSH_ERR_INVALID_ARGUMENT: return "PLPSH_ERR_INVALID_ARGUMENT";
@@ -319,7 +319,7 @@ size_t plpsh_workspace_bytes(int32_t heads_q, int32_t s, int32_t n) {
 }
 
 plpsh_status plpsh_attention_fwd(const void* q, const void* k, const void* v, void* o, int32_t batch,
-                                 int32_t heads_q, int32_t heads_kv, int32_t n, int32_t head_dim, plpsh_dtype dtype,
+                                 int32_t heads_q, int32_t heads_kv, int32_t n, int32_t head_dim, int32_t dtype,
                                  const double* sigma, int32_t s, uint64_t seed, int32_t causal, void* workspace,
                                  size_t workspace_bytes, void* stream) {
   plpsh_status r = check_qkv(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, causal);
@@ -336,7 +336,7 @@ plpsh_status plpsh_attention_fwd(const void* q, const void* k, const void* v, vo
 
 plpsh_status plpsh_attention_fwd_hashes(const void* q, const void* k, const void* v, void* o, int32_t batch,
                                         int32_t heads_q, int32_t heads_kv, int32_t n, int32_t head_dim,
-                                        plpsh_dtype dtype, const double* delta, const double* u, int32_t s,
+                                        int32_t dtype, const double* delta, const double* u, int32_t s,
                                         int32_t causal, void* workspace, size_t workspace_bytes, void* stream) {
   plpsh_status r = check_qkv(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, causal);
   if (r != PLPSH_OK) return r;
@@ -350,7 +350,7 @@ plpsh_status plpsh_attention_fwd_hashes(const void* q, const void* k, const void
 
 plpsh_status plpsh_fixed_blocks_fwd(const void* q, const void* k, const void* v, void* o, int32_t batch,
                                     int32_t heads_q, int32_t heads_kv, int32_t n, int32_t head_dim,
-                                    plpsh_dtype dtype, const int32_t* block, int32_t causal, void* workspace,
+                                    int32_t dtype, const int32_t* block, int32_t causal, void* workspace,
                                     size_t workspace_bytes, void* stream) {
   if (!block || heads_q < 1 || heads_q > 1024) return PLPSH_ERR_INVALID_ARGUMENT;
   std::vector<double> delta(heads_q), u(heads_q, 0.0);
@@ -364,7 +364,7 @@ plpsh_status plpsh_fixed_blocks_fwd(const void* q, const void* k, const void* v,
 
 namespace {
 plpsh_status fwd_bins(const void* q, const void* k, const void* v, void* o, int32_t batch, int32_t heads_q,
-                      int32_t heads_kv, int32_t n, int32_t head_dim, plpsh_dtype dtype, int32_t s, int32_t causal,
+                      int32_t heads_kv, int32_t n, int32_t head_dim, int32_t dtype, int32_t s, int32_t causal,
                       const void* bins, size_t bins_bytes, const double* delta, void* stream, bool literal,
                       float* lse = nullptr) {
   plpsh_status r = check_qkv(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, causal);
@@ -384,7 +384,7 @@ plpsh_status fwd_bins(const void* q, const void* k, const void* v, void* o, int3
 
 plpsh_status plpsh_attention_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse, int32_t batch,
                                      int32_t heads_q, int32_t heads_kv, int32_t n, int32_t head_dim,
-                                     plpsh_dtype dtype, int32_t s, int32_t causal, const void* bins,
+                                     int32_t dtype, int32_t s, int32_t causal, const void* bins,
                                      size_t bins_bytes, const double* delta, void* stream) {
   if ((!lse && batch > 0 && n > 0) || (reinterpret_cast<uintptr_t>(lse) & 3)) return PLPSH_ERR_INVALID_ARGUMENT;
   return fwd_bins(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, s, causal, bins, bins_bytes, delta,
@@ -393,7 +393,7 @@ plpsh_status plpsh_attention_fwd_lse(const void* q, const void* k, const void* v
 
 plpsh_status plpsh_attention_fwd_bins(const void* q, const void* k, const void* v, void* o, int32_t batch,
                                       int32_t heads_q, int32_t heads_kv, int32_t n, int32_t head_dim,
-                                      plpsh_dtype dtype, int32_t s, int32_t causal, const void* bins,
+                                      int32_t dtype, int32_t s, int32_t causal, const void* bins,
                                       size_t bins_bytes, const double* delta, void* stream) {
   return fwd_bins(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, s, causal, bins, bins_bytes, delta,
                   stream, false);
@@ -401,14 +401,14 @@ plpsh_status plpsh_attention_fwd_bins(const void* q, const void* k, const void* 
 
 plpsh_status plpsh_attention_fwd_literal(const void* q, const void* k, const void* v, void* o, int32_t batch,
                                          int32_t heads_q, int32_t heads_kv, int32_t n, int32_t head_dim,
-                                         plpsh_dtype dtype, int32_t s, int32_t causal, const void* bins,
+                                         int32_t dtype, int32_t s, int32_t causal, const void* bins,
                                          size_t bins_bytes, const double* delta, void* stream) {
   return fwd_bins(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, s, causal, bins, bins_bytes, delta,
                   stream, true);
 }
 
 plpsh_status plpsh_alibi_dense_fwd(const void* q, const void* k, const void* v, void* o, int32_t batch,
-                                   int32_t heads_q, int32_t heads_kv, int32_t n, int32_t head_dim, plpsh_dtype dtype,
+                                   int32_t heads_q, int32_t heads_kv, int32_t n, int32_t head_dim, int32_t dtype,
                                    const double* sigma, int32_t causal, void* stream) {
   plpsh_status r = check_qkv(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, causal);
   if (r != PLPSH_OK) return r;
@@ -556,7 +556,7 @@ size_t plpsh_attention_bwd_workspace_bytes(int32_t batch, int32_t heads_q, int32
 
 plpsh_status plpsh_attention_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                                  const float* lse, void* dq, void* dk, void* dv, int32_t batch, int32_t heads_q,
-                                 int32_t heads_kv, int32_t n, int32_t head_dim, plpsh_dtype dtype, int32_t s,
+                                 int32_t heads_kv, int32_t n, int32_t head_dim, int32_t dtype, int32_t s,
                                  int32_t causal, const void* bins, size_t bins_bytes, const double* delta,
                                  void* workspace, size_t workspace_bytes, void* stream) {
   plpsh_status r = check_qkv(q, k, v, dq, batch, heads_q, heads_kv, n, head_dim, dtype, causal);
