@@ -30,8 +30,9 @@
  *  - Every argument is validated before any HIP call; on a validation error
  *    nothing is launched and no output is touched.
  *  - Device pointers are caller-owned device memory (e.g. PyTorch tensors);
- *    the library allocates no device memory.  Host pointers are only read
- *    or written during the call.
+ *    the library allocates no device memory (its one static device array,
+ *    used by plpsh_attention_fwd_noalloc, is part of the loaded module).
+ *    Host pointers are only read or written during the call.
  *  - `stream` is a hipStream_t (NULL = the null stream).  Device work is
  *    enqueued on it and runs asynchronously; results are valid after the
  *    caller synchronises the stream.  PLPSH_ERR_HIP reports a launch or
@@ -197,6 +198,34 @@ plpsh_status plpsh_attention_fwd(const void* q, const void* k, const void* v, vo
                                  const double* sigma, int32_t s, uint64_t seed,
                                  int32_t causal, void* workspace, size_t workspace_bytes,
                                  void* stream);
+
+/* Limits of plpsh_attention_fwd_noalloc. */
+#define PLPSH_NOALLOC_MAX_HASHES 4096          /* heads_q * s */
+#define PLPSH_NOALLOC_BINS_BYTES (64u << 20)   /* plpsh_workspace_bytes(heads_q, s, n) */
+
+/*
+ * plpsh_attention_fwd_noalloc -- plpsh_attention_fwd for callers that cannot
+ * allocate memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, result and errors as
+ * plpsh_attention_fwd (bit-identical output for the same seed), minus the
+ * workspace: the bin buffer lives in a static device array of the library
+ * (PLPSH_NOALLOC_BINS_BYTES plus 16 bytes per hash), and the hashes reach
+ * the device as kernel arguments, so the call makes no device or host
+ * allocation (no hipMalloc, no pinned staging ring).
+ *   Limits: heads_q * s <= PLPSH_NOALLOC_MAX_HASHES and
+ *   plpsh_workspace_bytes(heads_q, s, n) <= PLPSH_NOALLOC_BINS_BYTES (a
+ *   32-head layer with s = 20 up to n = 16384 fits); beyond them the call
+ *   returns PLPSH_ERR_UNSUPPORTED and launches nothing.
+ *   The array is per device, held from library load until the process ends,
+ *   and shared by every call on that device: each call rewrites everything
+ *   it reads there (nothing needs clearing), and calls that overlap on one
+ *   device (concurrent streams, other threads) race on it -- order them.
+ */
+plpsh_status plpsh_attention_fwd_noalloc(const void* q, const void* k, const void* v, void* o,
+                                         int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                         int32_t n, int32_t head_dim, int32_t dtype,
+                                         const double* sigma, int32_t s, uint64_t seed,
+                                         int32_t causal, void* stream);
 
 /*
  * plpsh_attention_fwd_hashes -- as plpsh_attention_fwd with explicit hashes

@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     attention_literal,
     attention_lse,
     attention_hashes,
+    attention_noalloc,
     bins_from_hashes,
     bins_layout,
     draw_hashes,

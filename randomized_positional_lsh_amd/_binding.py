@@ -59,6 +59,8 @@ _SIGS = {
     "plpsh_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int]),
     "plpsh_attention_fwd": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                      _dp, _c_int, ctypes.c_uint64, _c_int, _vp, _c_sz, _vp]),
+    "plpsh_attention_fwd_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                             _dp, _c_int, ctypes.c_uint64, _c_int, _vp]),
     "plpsh_attention_fwd_hashes": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                             _dp, _dp, _c_int, _c_int, _vp, _c_sz, _vp]),
     "plpsh_attention_fwd_bins": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
@@ -281,6 +283,23 @@ def attention(q, k, v, sigma, s: int, seed: int = 0, causal: bool = False, out=N
                                   _torch_dtype_code(q), _ptr(sig), s, ctypes.c_uint64(seed & (2 ** 64 - 1)),
                                   int(bool(causal)), ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream))
     _check(st, "plpsh_attention_fwd")
+    return out
+
+
+def attention_noalloc(q, k, v, sigma, s: int, seed: int = 0, causal: bool = False, out=None, stream=None):
+    """plpsh_attention_fwd with the bin buffer in the library's static device
+    array (plpsh_attention_fwd_noalloc): no workspace, no allocation inside
+    the call (`out` is allocated here only when not supplied)."""
+    B, Hq, Hkv, n, d = _qkv_shapes(q, k, v)
+    sig = _f64(sigma).reshape(-1)
+    if sig.size != Hq:
+        raise ValueError("sigma must have one entry per query head")
+    out = _out_like(out, q, stream=stream)
+    st = _lib.plpsh_attention_fwd_noalloc(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                          ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()), B, Hq, Hkv,
+                                          n, d, _torch_dtype_code(q), _ptr(sig), s,
+                                          ctypes.c_uint64(seed & (2 ** 64 - 1)), int(bool(causal)), _stream(stream))
+    _check(st, "plpsh_attention_fwd_noalloc")
     return out
 
 

@@ -131,21 +131,30 @@ plpsh_status check_qkv(const void* q, const void* k, const void* v, void* o, int
   return PLPSH_OK;
 }
 
+constexpr int kMaxHeads = 1024;  // check_qkv rejects more query heads
+
+// Query heads by cost, largest first (ties by head index): cost[h] is the
+// sum over head h's hashes of min(delta, n), which grows with its key window.
+void order_by_cost(int hq, const double* cost, uint16_t* order) {
+  for (int h = 0; h < hq; ++h) order[h] = static_cast<uint16_t>(h);
+  std::sort(order, order + hq, [&](uint16_t a, uint16_t b) { return cost[a] > cost[b] || (cost[a] == cost[b] && a < b); });
+}
+
 // Launch the attention kernel on a computed bin buffer.  Heads with the
 // widest bins (largest key windows) are scheduled first when delta is known.
 plpsh_status attention_on_bins(const void* q, const void* k, const void* v, void* o, int batch, int hq, int hkv,
                                int n, int d, int dtype, const double* delta, int s, int causal, const void* bins,
                                hipStream_t st, bool literal = false, float* lse = nullptr) {
-  std::vector<uint16_t> order(hq);
-  std::iota(order.begin(), order.end(), 0);
-  if (delta) {
-    std::vector<double> cost(hq, 0.0);
-    for (int h = 0; h < hq; ++h)
+  uint16_t order[kMaxHeads];
+  double cost[kMaxHeads];
+  for (int h = 0; h < hq; ++h) {
+    cost[h] = 0.0;
+    if (delta)
       for (int i = 0; i < s; ++i) cost[h] += std::min(delta[h * s + i], static_cast<double>(n));
-    std::stable_sort(order.begin(), order.end(), [&](uint16_t a, uint16_t b) { return cost[a] > cost[b]; });
   }
-  if (hip_failed(plpsh::launch_plsh_fwd(q, k, v, o, batch, hq, hkv, n, d, dtype, s, causal, bins, order.data(),
-                                        literal, lse, st),
+  order_by_cost(hq, cost, order);
+  if (hip_failed(plpsh::launch_plsh_fwd(q, k, v, o, batch, hq, hkv, n, d, dtype, s, causal, bins, order, literal,
+                                        lse, st),
                  "attention kernel launch"))
     return PLPSH_ERR_HIP;
   return PLPSH_OK;
@@ -599,3 +608,90 @@ plpsh_status plpsh_attention_bwd(const void* q, const void* k, const void* v, co
 
 }  // extern "C"
 
+// ---- attention with no allocation: the bin buffer in a static device array
+
+namespace {
+
+// The library's own scratch: (delta, u) pairs, then a bin buffer of up to
+// PLPSH_NOALLOC_BINS_BYTES.  Every device holds its own copy at its own
+// address from module load until the process ends.  In host code `scratch`
+// only names the symbol: its device address comes from hipGetSymbolAddress.
+constexpr size_t kNoallocHashBytes = static_cast<size_t>(PLPSH_NOALLOC_MAX_HASHES) * 2 * sizeof(double);
+__device__ __align__(256) unsigned char scratch[kNoallocHashBytes + PLPSH_NOALLOC_BINS_BYTES];
+
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch (looked up once per device, with
+// that device current).
+plpsh_status scratch_ptr(char** out) {
+  int dev = 0;
+  if (hip_failed(hipGetDevice(&dev), "hipGetDevice")) return PLPSH_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return PLPSH_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hip_failed(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)")) return PLPSH_ERR_HIP;
+    if (!p) return PLPSH_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return PLPSH_OK;
+}
+
+// (delta, u) pairs reach the device as kernel arguments (copied by the
+// runtime at launch), kStagePairs per launch: no host staging memory.
+constexpr int kStagePairs = 224;
+struct StageArgs {
+  int32_t first, count;
+  double du[2 * kStagePairs];
+};
+static_assert(sizeof(StageArgs) <= 3600, "kernel arguments stay under 4 KB");
+
+__global__ __launch_bounds__(2 * kStagePairs) void stage_hashes_kernel(StageArgs a, double* __restrict__ dst) {
+  const int t = static_cast<int>(threadIdx.x);
+  if (t < 2 * a.count) dst[2 * static_cast<size_t>(a.first) + t] = a.du[t];
+}
+
+}  // namespace
+
+extern "C" plpsh_status plpsh_attention_fwd_noalloc(const void* q, const void* k, const void* v, void* o,
+                                                    int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t n,
+                                                    int32_t head_dim, int32_t dtype, const double* sigma, int32_t s,
+                                                    uint64_t seed, int32_t causal, void* stream) {
+  plpsh_status r = check_qkv(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, causal);
+  if (r != PLPSH_OK) return r;
+  if (!valid_hs(heads_q, s) || !valid_sigma(sigma, heads_q)) return PLPSH_ERR_INVALID_ARGUMENT;
+  if (batch == 0 || n == 0) return PLPSH_OK;
+  const int hs = heads_q * s;
+  if (hs > PLPSH_NOALLOC_MAX_HASHES) return PLPSH_ERR_UNSUPPORTED;
+  if (plpsh::bins_layout(heads_q, s, n).total > PLPSH_NOALLOC_BINS_BYTES) return PLPSH_ERR_UNSUPPORTED;
+  char* base = nullptr;
+  if ((r = scratch_ptr(&base)) != PLPSH_OK) return r;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  double* du = reinterpret_cast<double*>(base);
+  void* bins = base + kNoallocHashBytes;
+
+  // hashes drawn straight into the launch arguments; per-head costs on the way
+  double cost[kMaxHeads] = {};
+  StageArgs a;
+  for (int first = 0; first < hs; first += kStagePairs) {
+    a.first = first;
+    a.count = std::min(kStagePairs, hs - first);
+    for (int t = 0; t < a.count; ++t) {
+      const int h = (first + t) / s, i = (first + t) - h * s;
+      plpsh::draw_hash(seed, h, i, sigma[h], &a.du[2 * t], &a.du[2 * t + 1]);
+      cost[h] += std::min(a.du[2 * t], static_cast<double>(n));
+    }
+    hipLaunchKernelGGL(stage_hashes_kernel, dim3(1), dim3(2 * kStagePairs), 0, st, a, du);
+    if (hip_failed(hipGetLastError(), "hash staging kernel launch")) return PLPSH_ERR_HIP;
+  }
+  if (hip_failed(plpsh::launch_bins(du, heads_q, s, n, bins, st), "bin kernel launch")) return PLPSH_ERR_HIP;
+  uint16_t order[kMaxHeads];
+  order_by_cost(heads_q, cost, order);
+  if (hip_failed(plpsh::launch_plsh_fwd(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, s, causal, bins,
+                                        order, false, nullptr, st),
+                 "attention kernel launch"))
+    return PLPSH_ERR_HIP;
+  return PLPSH_OK;
+}

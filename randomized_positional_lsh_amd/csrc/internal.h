@@ -50,8 +50,10 @@ struct BinsLayout {
 };
 BinsLayout bins_layout(int heads, int s, int n);
 
-// Host draw (SplitMix64 counter mode, see plpsh.h).
+// Host draw (SplitMix64 counter mode, see plpsh.h): all heads * s hashes,
+// or hash i of head h alone (the same value, the streams are counter-based).
 void draw_hashes(uint64_t seed, int heads, int s, const double* sigma, double* delta, double* u);
+void draw_hash(uint64_t seed, int h, int i, double sigma, double* delta, double* u);
 
 // Device launches.  `du` points to heads*s interleaved (delta, u) pairs in
 // device-readable memory.

@@ -24,21 +24,21 @@ inline double unit_open(uint64_t z) {
 
 }  // namespace
 
-void draw_hashes(uint64_t seed, int heads, int s, const double* sigma, double* delta, double* u) {
-  for (int h = 0; h < heads; ++h) {
-    for (int i = 0; i < s; ++i) {
-      double U[3];
-      for (int k = 0; k < 3; ++k) {
-        const uint64_t c = (static_cast<uint64_t>(h) << 32) | (static_cast<uint64_t>(i) << 2) |
-                           static_cast<uint64_t>(k);
-        U[k] = unit_open(mix64(seed + (c + 1) * kGamma));
-      }
-      const double t = (-std::log(U[0])) - std::log(U[1]);
-      const double dl = sigma[h] * t;
-      delta[h * s + i] = dl;
-      u[h * s + i] = dl * U[2];
-    }
+void draw_hash(uint64_t seed, int h, int i, double sigma, double* delta, double* u) {
+  double U[3];
+  for (int k = 0; k < 3; ++k) {
+    const uint64_t c = (static_cast<uint64_t>(h) << 32) | (static_cast<uint64_t>(i) << 2) | static_cast<uint64_t>(k);
+    U[k] = unit_open(mix64(seed + (c + 1) * kGamma));
   }
+  const double t = (-std::log(U[0])) - std::log(U[1]);
+  const double dl = sigma * t;
+  *delta = dl;
+  *u = dl * U[2];
+}
+
+void draw_hashes(uint64_t seed, int heads, int s, const double* sigma, double* delta, double* u) {
+  for (int h = 0; h < heads; ++h)
+    for (int i = 0; i < s; ++i) draw_hash(seed, h, i, sigma[h], &delta[h * s + i], &u[h * s + i]);
 }
 
 }  // namespace plpsh

@@ -275,3 +275,27 @@ def test_binding_checks_caller_outputs_before_the_c_abi():
         P.attention_bwd(qb, kb, kb, qb, qb, lse, bins, dv=torch.zeros_like(kb).float())
     with pytest.raises(ValueError):
         P.attention_lse(qb, kb, kb, bins, lse=lse[:, :, :10])
+
+
+def test_noalloc_validation_and_limits():
+    """The no-allocation entry point validates like plpsh_attention_fwd and
+    rejects problems beyond its static array before any HIP call."""
+    lib = B.raw()
+    sig2 = np.array([2.0, 4.0])
+
+    def call(q=FAKE, o=FAKE, batch=1, hq=2, hkv=1, n=64, d=64, dtype=1, sigma=sig2, s=4, causal=0):
+        sg = np.ascontiguousarray(sigma, dtype=np.float64)
+        return lib.plpsh_attention_fwd_noalloc(q, FAKE, FAKE, o, batch, hq, hkv, n, d, dtype, B._ptr(sg), s, 0,
+                                               causal, None)
+    assert call(q=None) == B.INVALID_ARGUMENT
+    assert call(s=0) == B.INVALID_ARGUMENT
+    assert call(sigma=np.array([2.0, -1.0])) == B.INVALID_ARGUMENT
+    assert call(dtype=5) == B.INVALID_ARGUMENT
+    assert call(d=96) == B.UNSUPPORTED
+    assert call(batch=0) == B.OK and call(n=0) == B.OK          # empty: nothing launched
+    # more hashes than the array holds (heads_q * s > 4096)
+    assert call(hq=64, hkv=1, sigma=np.full(64, 2.0), s=65) == B.UNSUPPORTED
+    # a bin buffer larger than the array (32 heads, s = 32, n = 131072: about 537 MB)
+    assert call(hq=32, hkv=8, sigma=np.full(32, 2.0), s=32, n=131072) == B.UNSUPPORTED
+    # the 32-head, s = 20, n = 16384 layer fits
+    assert P.workspace_bytes(32, 20, 16384) <= 64 << 20
