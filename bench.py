@@ -8,15 +8,24 @@ plpsh_attention_fwd does).  Default workload: one Mistral-7B-shaped
 attention layer (batch 1, 32 query / 8 KV heads, n = 16384, head_dim 128,
 bf16, causal, s = 20, sigma_h = 2^(8(h+1)/32)), synthetic N(0, 1) inputs.
 
+The timed loop (`value`, `ms_per_step`) records nothing but the steps.
+Separate passes afterwards give the per-step distribution (one event per
+step boundary) and the attention kernel's duration (an event pair around
+each launch, on the stream it runs on).
+
 Prints ONE JSON line.  Besides the contract fields it carries:
-  roofline     : the attention kernel against the HBM roofline (algorithmic
-                 bytes = Q, K, V read once + O written once, per launch,
-                 divided by the kernel's mean duration from HIP events
-                 recorded around it on its stream in 10 evenly spaced steps
-                 of the timed loop); also the same kernel with the L2 and
-                 last-level cache evicted before each launch
+  step_ms      : median, p10, p90 of the step time (separate pass)
+  roofline     : the attention kernel against the HBM roofline: algorithmic
+                 bytes (Q, K, V read once + O written once, per launch)
+                 divided by the kernel's median duration with the L2 and the
+                 last-level cache evicted before each launch (the roofline
+                 figure: a step's inputs are not cache-resident in a model);
+                 the back-to-back (warm-cache) figures side by side
+  workloads    : tiny, small, qwen3, long: tokens/s of the step, the
+                 kernel's cold- and warm-cache median, cold-cache HBM fraction
   cpu_baseline : the fp64 oracle timed on a bounded sample of the same
-                 workload on the host cores
+                 workload by a pool of worker processes (one per core of the
+                 host's share, one BLAS thread each)
   dense_alibi  : exact ALiBi (plpsh_alibi_dense_fwd) at the same n
   literal      : the same step with the attention computed as one short
                  attention per hash (plpsh_attention_fwd_literal, the
@@ -145,95 +154,146 @@ class Runner:
             raise RuntimeError(self.P.status_string(st))
 
 
-def time_steps(run, steps, warmup, samples=10):
-    """Wall time of `steps` back-to-back steps, and the attention kernel's
-    duration (ms) from HIP events recorded around it on its stream in
-    `samples` evenly spaced steps of the same timed loop (all steps if
-    samples >= steps, none if 0).  An event pair between the two kernels of
-    a step costs the stream about 7 us on MI355X, so recording one in every
-    step would add that much to every step's time."""
+def time_steps(run, steps, warmup):
+    """Wall time of `steps` back-to-back steps (nothing else is recorded on
+    the stream in between)."""
     import torch
     for _ in range(warmup):
         run.bins()
         run.attn()
     torch.cuda.synchronize()
-    every = 0 if samples <= 0 else max(1, steps // samples)
-    marks = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for i in range(steps) if every and i % every == 0}
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(steps):
+        run.bins()
+        run.attn()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def pct(x) -> dict:
+    import numpy as np
+    return {"median": round(float(np.median(x)), 5), "p10": round(float(np.percentile(x, 10)), 5),
+            "p90": round(float(np.percentile(x, 90)), 5)}
+
+
+def step_times(run, steps):
+    """Per-step durations (ms) from one event at every step boundary."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
     for i in range(steps):
         run.bins()
-        ab = marks.get(i)
-        if ab is None:
-            run.attn()
-        else:
-            ab[0].record()
-            run.attn()
-            ab[1].record()
+        run.attn()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern = [a.elapsed_time(b) for a, b in marks.values()]  # ms
-    return wall, kern
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
 
 
-def cold_kernel_ms(run, reps=20):
-    """Mean attention-kernel time with the L2 and the 256 MB last-level
-    cache evicted before every launch: a 512 MiB buffer is overwritten on the
-    same stream between launches, outside the events."""
-    import numpy as np
+def kernel_times(run, reps, cold):
+    """Durations (ms) of the attention kernel alone on the current bins, an
+    event pair around each launch on its stream.  cold: a 512 MiB buffer is
+    overwritten on the same stream before every launch, outside the events,
+    which evicts the L2 and the 256 MB last-level cache."""
     import torch
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=run.q.device)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=run.q.device) if cold else None
+    for _ in range(3):
+        run.attn()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in ev:
-        scratch.fill_(1)
+        if scratch is not None:
+            scratch.fill_(1)
         a.record()
         run.attn()
         b.record()
     torch.cuda.synchronize()
     del scratch
-    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def _cpu_worker(job):
+    """One worker of the CPU baseline: oracle tasks (64-row block, head) from
+    the memory-mapped inputs, with one BLAS thread, from a common start time
+    until `seconds` have passed."""
+    import numpy as np
+    import threadpoolctl
+    threadpoolctl.threadpool_limits(1)
+    import oracle
+    d, tasks, causal, grp, seconds, t_start = job
+    q = np.load(os.path.join(d, "q.npy"), mmap_mode="r")
+    k = np.load(os.path.join(d, "k.npy"), mmap_mode="r")
+    v = np.load(os.path.join(d, "v.npy"), mmap_mode="r")
+    delta = np.load(os.path.join(d, "delta.npy"))
+    u = np.load(os.path.join(d, "u.npy"))
+    while time.time() < t_start:
+        time.sleep(0.01)
+    t0 = time.time()
+    rows = done = 0
+    for blk, h in tasks:
+        out, _ = oracle.plsh_attention_rowblocks(q[h], k[h // grp], v[h // grp], delta[h], u[h], causal,
+                                                 row_block=64, blocks=[blk])
+        rows += out.shape[0]
+        done += 1
+        if time.time() - t0 >= seconds:
+            break
+    return rows, done, time.time() - t0
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(W, q, k, v, delta, u, seconds):
-    """The oracle, as it stands, on a bounded sample of the workload: 64-row
-    blocks taken round-robin over all heads (so every sigma is represented)
-    until `seconds` of wall time have passed."""
+    """The oracle, as it stands, on a bounded sample of the workload, by a
+    pool of worker processes, one per core of the host's share (at most 16,
+    the host share of one GPU), each with one BLAS thread: (64-row block,
+    head) tasks, blocks in random order and every head per block (so every
+    sigma is represented), dealt round-robin; every worker runs for `seconds`
+    from a common start.  Workers are started fresh (spawn) and read the
+    inputs from memory-mapped files."""
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+    from concurrent.futures import ProcessPoolExecutor
     import numpy as np
-    import oracle
+    nproc = len(os.sched_getaffinity(0))
+    workers = max(1, min(nproc, 16))
+    d = tempfile.mkdtemp(prefix="plpsh_cpu_", dir="/dev/shm" if os.path.isdir("/dev/shm") else None)
     try:
-        import threadpoolctl
-        cores = sum(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()
-                    if i.get("user_api") == "blas") or 1
-    except Exception:
-        cores = 1
-    rng = np.random.default_rng(0)
-    nblk = (W.n + 63) // 64
-    order = rng.permutation(nblk)
-    grp = W.heads_q // W.heads_kv
-    kh = [k[0, g].float().cpu().numpy().astype(np.float64) for g in range(W.heads_kv)]
-    vh = [v[0, g].float().cpu().numpy().astype(np.float64) for g in range(W.heads_kv)]
-    qh = [q[0, h].float().cpu().numpy().astype(np.float64) for h in range(W.heads_q)]
-    rows = 0
-    tasks = 0
-    t0 = time.perf_counter()
-    for blk in order:
-        for h in range(W.heads_q):
-            out, rr = oracle.plsh_attention_rowblocks(qh[h], kh[h // grp], vh[h // grp], delta[h], u[h], W.causal,
-                                                      row_block=64, blocks=[int(blk)])
-            rows += out.shape[0]
-            tasks += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    el = time.perf_counter() - t0
-    rows_per_s = rows / el
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            np.save(os.path.join(d, f"{name}.npy"), t[0].float().cpu().numpy())
+        np.save(os.path.join(d, "delta.npy"), np.asarray(delta, dtype=np.float64))
+        np.save(os.path.join(d, "u.npy"), np.asarray(u, dtype=np.float64))
+        rng = np.random.default_rng(0)
+        order = rng.permutation((W.n + 63) // 64)
+        tasks = [(int(blk), h) for blk in order for h in range(W.heads_q)]
+        grp = W.heads_q // W.heads_kv
+        t_start = time.time() + 5.0  # after every worker has started and mapped its inputs
+        jobs = [(d, tasks[i::workers], W.causal, grp, seconds, t_start) for i in range(workers)]
+        # a worker that dies raises here (BrokenProcessPool) instead of hanging
+        with ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as pool:
+            res = list(pool.map(_cpu_worker, jobs))
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+    rows = sum(r[0] for r in res)
+    done = sum(r[1] for r in res)
+    el = max(r[2] for r in res)
     return {
-        "value": rows_per_s / W.heads_q,  # a token needs one output row in every head
+        "value": rows / el / W.heads_q,  # a token needs one output row in every head
         "unit": "tokens/s",
-        "cores": int(cores),
+        "cores": workers,
         "kind": "oracle",
-        "sample": f"{tasks} (head, 64-row block) tasks = {rows} output rows over all {W.heads_q} heads "
-                  f"in {el:.1f} s (banded fp64 oracle, hash seed {W.hash_seed})",
+        "nproc": nproc,
+        "cpu_model": cpu_model(),
+        "sample": f"{done} (head, 64-row block) tasks = {rows} output rows over all {W.heads_q} heads in "
+                  f"{el:.1f} s by {workers} worker processes with 1 BLAS thread each (banded fp64 oracle, "
+                  f"hash seed {W.hash_seed})",
     }
 
 
@@ -333,7 +393,7 @@ def crossover(P, synth, dev, ns, steps=5):
         W = synth.Workload(f"mistral-n{n}", 1, 32, 8, n, 128, "bf16", synth.alibi_sigmas(32), 20, True, 0, 1003)
         q, k, v = synth.qkv_torch(1, 32, 8, n, 128, "bf16", 1003, dev)
         run = Runner(P, W, q, k, v, torch.empty_like(q), dev)
-        wall, _ = time_steps(run, steps, 2, samples=0)
+        wall = time_steps(run, steps, 2)
         dms = dense_alibi(P, W, q, k, v, steps=steps, warmup=2)
         out["n"].append(n)
         out["plsh_ms"].append(round(1e3 * wall / steps, 4))
@@ -353,22 +413,45 @@ def long_point(P, synth, dev, dense_ms, steps=5):
     """The long-context workload (n = 131072, s = 32, causal, Mistral head
     layout) as one step of the whole path, against dense exact ALiBi at the
     same n (the dense kernel does not depend on s)."""
+    import numpy as np
     import torch
     W = synth.WORKLOADS["long"]
     q, k, v = synth.qkv_torch(W.batch, W.heads_q, W.heads_kv, W.n, W.head_dim, W.dtype, W.data_seed, dev)
     run = Runner(P, W, q, k, v, torch.empty_like(q), dev)
-    wall, kern = time_steps(run, steps, 2, samples=steps)
+    wall = time_steps(run, steps, 2)
     ms = 1e3 * wall / steps
+    kms = float(np.median(kernel_times(run, 5, cold=True)))
     del q, k, v, run
     torch.cuda.empty_cache()
-    kms = sum(kern) / len(kern)
     out = {"workload": "long-context", "n": W.n, "s": W.s, "plsh_ms": round(ms, 4),
-           "kernel_ms": round(kms, 4), "tokens_per_s": round(W.batch * W.n / (ms * 1e-3), 1),
-           "hbm_frac": round(algorithmic_bytes(W) / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+           "kernel_ms_cold_cache": round(kms, 4), "tokens_per_s": round(W.batch * W.n / (ms * 1e-3), 1),
+           "hbm_frac_cold_cache": round(algorithmic_bytes(W) / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     if dense_ms is not None:
         out["dense_ms"] = round(dense_ms, 4)
         out["speedup_plsh_vs_dense"] = round(dense_ms / ms, 2)
     return out
+
+
+def workload_point(P, synth, dev, name, steps=20):
+    """One workload as a step of the whole path: tokens/s of the step, the
+    attention kernel's median with caches evicted and back to back, and the
+    cold-cache HBM fraction."""
+    import numpy as np
+    import torch
+    W = synth.WORKLOADS[name]
+    q, k, v = synth.qkv_torch(W.batch, W.heads_q, W.heads_kv, W.n, W.head_dim, W.dtype, W.data_seed, dev)
+    run = Runner(P, W, q, k, v, torch.empty_like(q), dev)
+    wall = time_steps(run, steps, 5)
+    ms = 1e3 * wall / steps
+    cold = float(np.median(kernel_times(run, 10, cold=True)))
+    warm = float(np.median(kernel_times(run, 10, cold=False)))
+    del q, k, v, run
+    torch.cuda.empty_cache()
+    return {"batch": W.batch, "heads_q": W.heads_q, "heads_kv": W.heads_kv, "n": W.n, "head_dim": W.head_dim,
+            "dtype": W.dtype, "s": W.s, "causal": W.causal, "step_ms": round(ms, 5),
+            "tokens_per_s": round(W.batch * W.n / (ms * 1e-3), 1), "kernel_ms_cold_cache": round(cold, 5),
+            "kernel_ms_warm": round(warm, 5),
+            "hbm_frac_cold_cache": round(algorithmic_bytes(W) / (cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def convergence(P, dev, n=131072, sigma=256.0, ss=(2, 4, 8, 16, 32, 64, 128), seeds=3, max_steps=400):
@@ -429,6 +512,7 @@ def main():
     ap.add_argument("--no-convergence", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-literal", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true", help="only run a 1 GiB device copy (counter scaling)")
     args = ap.parse_args()
 
@@ -455,13 +539,18 @@ def main():
     q, k, v = synth.qkv_torch(W.batch, W.heads_q, W.heads_kv, W.n, W.head_dim, W.dtype, W.data_seed, dev)
     o = torch.empty_like(q)
     run = Runner(P, W, q, k, v, o, dev)
-    wall, kern = time_steps(run, args.steps, args.warmup)
+    wall = time_steps(run, args.steps, args.warmup)
     ms_step = 1e3 * wall / args.steps
     tokens = W.batch * W.n
     value = tokens / (wall / args.steps)
-    kern_ms = float(np.mean(kern))
-    log(f"step {ms_step:.4f} ms, attention kernel {kern_ms:.4f} ms (p10 {np.percentile(kern, 10):.4f}, "
-        f"p90 {np.percentile(kern, 90):.4f})")
+    log(f"step {ms_step:.4f} ms ({args.steps} timed steps)")
+    steps_ms = step_times(run, args.steps)
+    warm = kernel_times(run, 50, cold=False)
+    cold = kernel_times(run, 50, cold=True)
+    kern_ms = float(np.median(cold))
+    warm_ms = float(np.median(warm))
+    log(f"step median {np.median(steps_ms):.4f} ms; attention kernel median {kern_ms:.4f} ms with caches evicted, "
+        f"{warm_ms:.4f} ms back to back")
 
     delta = run.delta.reshape(W.heads_q, W.s).copy()
     u = run.u.reshape(W.heads_q, W.s).copy()
@@ -475,15 +564,14 @@ def main():
             traffic = int(tr["bytes_per_launch"])
     flops = useful_flops(W, P, run.ws)
     tflops = flops / (kern_ms * 1e-3) / 1e12
-    cold_ms = cold_kernel_ms(run)
-    log(f"attention kernel with caches evicted before each launch {cold_ms:.4f} ms")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "plpsh fwd_kernel (attention)", "kernel_ms": round(kern_ms, 5),
-                "algorithmic_bytes": abytes,
+                "kernel": "plpsh fwd_kernel (attention)", "cache": "L2 and last-level cache evicted before each launch",
+                "kernel_ms": round(kern_ms, 5), "kernel_ms_pct": pct(cold), "algorithmic_bytes": abytes,
                 "useful_tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                "kernel_ms_cold_cache": round(cold_ms, 5),
-                "frac_cold_cache": round(abytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                "kernel_ms_warm": round(warm_ms, 5), "kernel_ms_warm_pct": pct(warm),
+                "frac_warm": round(abytes / (warm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "outside_kernel_ms": round(ms_step - warm_ms, 5)}
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -492,6 +580,7 @@ def main():
         "config": {"workload": f"{W.name}-layer", "batch": W.batch, "heads_q": W.heads_q, "heads_kv": W.heads_kv,
                    "n": W.n, "head_dim": W.head_dim, "s": W.s, "causal": W.causal,
                    "sigma": "2^(8(h+1)/H)", "parallelism": "single GPU"},
+        "step_ms": pct(steps_ms),
         "roofline": roofline,
     }
     if W.dtype == "bf16" and not args.no_backward:
@@ -499,8 +588,8 @@ def main():
         log(f"backward {line['backward']}")
     if not args.no_literal:
         lms = literal(run)
-        line["literal"] = {"kernel_ms": round(lms, 4), "fused_kernel_ms": round(kern_ms, 4),
-                           "slowdown_vs_fused": round(lms / kern_ms, 2)}
+        line["literal"] = {"kernel_ms": round(lms, 4), "fused_kernel_ms": round(warm_ms, 4),
+                           "slowdown_vs_fused": round(lms / warm_ms, 2)}
         log(f"literal per-hash attention kernel {lms:.4f} ms")
     if not args.no_dense:
         dms = dense_alibi(P, W, q, k, v)
@@ -512,6 +601,12 @@ def main():
                                 "block": "round(2 sigma_h)", "block_min": int(block.min()),
                                 "block_max": int(block.max())}
         log(f"fixed blocks {fms:.4f} ms")
+    if not args.no_workloads:
+        line["workloads"] = {}
+        for name in ("tiny", "small", "qwen3", "long"):
+            if name != W.name:
+                line["workloads"][name] = workload_point(P, synth, dev, name)
+                log(f"workload {name} {line['workloads'][name]}")
     if not args.no_crossover and W.name == "mistral":
         del o
         line["crossover"] = crossover(P, synth, dev, [512, 1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072])
