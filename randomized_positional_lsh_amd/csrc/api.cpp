@@ -26,41 +26,89 @@ bool hip_failed(hipError_t e, const char* what) {
 }
 
 using plpsh::kMaxDevices;
-constexpr int kSlots = 8;
-constexpr size_t kSlotBytes = static_cast<size_t>(PLPSH_MAX_HASHES) * 2 * sizeof(double);
+constexpr int kGroupSlots = 16;  // calls per event
+constexpr int kGroups = 2;
+constexpr int kSlots = kGroups * kGroupSlots;
+constexpr size_t kSlotQuantum = 64 << 10;  // slot sizes: multiples of 64 KB (4096 hashes)
 
 // Per-device ring of pinned host slots holding (delta, u) pairs that the bin
-// kernel reads directly (zero copy).  A slot is reused only after the event
-// recorded behind the kernel that read it has completed.
+// kernel reads directly (zero copy).  A slot is reused only after an event
+// recorded behind the kernel that read it has completed.  An event recorded
+// on a stream holds every later launch on it behind the marker, which costs
+// the stream several microseconds, so on the null stream one event covers a
+// group of up to kGroupSlots consecutive calls: the group closes (its event
+// recorded behind its last kernel) when it is full or a call comes on
+// another stream.  Calls on other streams, which the caller may destroy
+// before a later call, close their group at once.
 struct Staging {
   std::mutex mu;
-  bool ready = false;
-  char* host = nullptr;   // kSlots * kSlotBytes, pinned
+  size_t slot_bytes = 0;  // per slot: the largest request so far, rounded up
+  char* host = nullptr;   // kSlots * slot_bytes, pinned
   char* dev = nullptr;    // device view of `host`
-  hipEvent_t ev[kSlots] = {};
-  bool used[kSlots] = {};
-  int next = 0;
+  bool events = false;
+  hipEvent_t ev[kGroups] = {};
+  bool pending[kGroups] = {};  // event recorded and not yet waited for
+  int next = 0;                // next slot
+  int open_calls = 0;          // calls in the open group (the group of slot next - 1)
+  hipStream_t open_stream = nullptr;
 };
 Staging g_staging[kMaxDevices];
 
-bool staging_acquire(Staging& S, int* slot) {
-  if (!S.ready) {
+bool staging_close(Staging& S) {
+  if (S.open_calls == 0) return true;
+  const int g = ((S.next + kSlots - 1) % kSlots) / kGroupSlots;
+  if (hip_failed(hipEventRecord(S.ev[g], S.open_stream), "hipEventRecord(staging group)")) return false;
+  S.pending[g] = true;
+  S.open_calls = 0;
+  return true;
+}
+
+bool staging_acquire(Staging& S, hipStream_t st, size_t bytes, int* slot) {
+  if (!S.events) {
+    for (int i = 0; i < kGroups; ++i)
+      if (hip_failed(hipEventCreateWithFlags(&S.ev[i], hipEventDisableTiming), "hipEventCreateWithFlags"))
+        return false;
+    S.events = true;
+  }
+  if (bytes > S.slot_bytes) {
+    // grow the ring: every kernel reading the old one has completed first
+    if (!staging_close(S)) return false;
+    for (int g = 0; g < kGroups; ++g)
+      if (S.pending[g]) {
+        if (hip_failed(hipEventSynchronize(S.ev[g]), "hipEventSynchronize(staging group)")) return false;
+        S.pending[g] = false;
+      }
+    if (S.host && hip_failed(hipHostFree(S.host), "hipHostFree(staging)")) return false;
+    S.host = S.dev = nullptr;
+    S.slot_bytes = 0;
+    const size_t sb = (bytes + kSlotQuantum - 1) / kSlotQuantum * kSlotQuantum;
     void* p = nullptr;
-    if (hip_failed(hipHostMalloc(&p, kSlots * kSlotBytes, hipHostMallocMapped | hipHostMallocCoherent),
+    if (hip_failed(hipHostMalloc(&p, kSlots * sb, hipHostMallocMapped | hipHostMallocCoherent),
                    "hipHostMalloc(staging)"))
       return false;
     void* d = nullptr;
-    if (hip_failed(hipHostGetDevicePointer(&d, p, 0), "hipHostGetDevicePointer(staging)")) return false;
-    for (int i = 0; i < kSlots; ++i)
-      if (hip_failed(hipEventCreateWithFlags(&S.ev[i], hipEventDisableTiming), "hipEventCreateWithFlags"))
-        return false;
+    if (hip_failed(hipHostGetDevicePointer(&d, p, 0), "hipHostGetDevicePointer(staging)")) {
+      (void)hipHostFree(p);
+      return false;
+    }
     S.host = static_cast<char*>(p);
     S.dev = static_cast<char*>(d);
-    S.ready = true;
+    S.slot_bytes = sb;
+    S.next = 0;
+  }
+  // a call on another stream closes the open group and starts the next one,
+  // so that every group's event covers all of its calls
+  if (S.open_calls > 0 && st != S.open_stream) {
+    if (!staging_close(S)) return false;
+    S.next = (S.next + kGroupSlots - 1) / kGroupSlots * kGroupSlots % kSlots;
   }
   const int i = S.next;
-  S.next = (S.next + 1) % kSlots;
-  if (S.used[i] && hip_failed(hipEventSynchronize(S.ev[i]), "hipEventSynchronize(staging slot)")) return false;
+  const int g = i / kGroupSlots;
+  if (i % kGroupSlots == 0 && S.pending[g]) {
+    if (hip_failed(hipEventSynchronize(S.ev[g]), "hipEventSynchronize(staging group)")) return false;
+    S.pending[g] = false;
+  }
+  S.next = (i + 1) % kSlots;
   *slot = i;
   return true;
 }
@@ -96,18 +144,22 @@ plpsh_status run_bins(int heads, int s, int n, const double* delta, const double
   if (dev < 0 || dev >= kMaxDevices) return PLPSH_ERR_UNSUPPORTED;
   Staging& S = g_staging[dev];
   std::lock_guard<std::mutex> lock(S.mu);
-  int slot = 0;
-  if (!staging_acquire(S, &slot)) return PLPSH_ERR_HIP;
-  double* du = reinterpret_cast<double*>(S.host + slot * kSlotBytes);
   const int hs = heads * s;
+  int slot = 0;
+  if (!staging_acquire(S, st, static_cast<size_t>(hs) * 2 * sizeof(double), &slot)) return PLPSH_ERR_HIP;
+  double* du = reinterpret_cast<double*>(S.host + slot * S.slot_bytes);
   for (int t = 0; t < hs; ++t) {
     du[2 * t] = delta[t];
     du[2 * t + 1] = u[t];
   }
-  const double* ddu = reinterpret_cast<const double*>(S.dev + slot * kSlotBytes);
+  const double* ddu = reinterpret_cast<const double*>(S.dev + slot * S.slot_bytes);
   if (hip_failed(plpsh::launch_bins(ddu, heads, s, n, bins, st), "bin kernel launch")) return PLPSH_ERR_HIP;
-  if (hip_failed(hipEventRecord(S.ev[slot], st), "hipEventRecord(staging slot)")) return PLPSH_ERR_HIP;
-  S.used[slot] = true;
+  S.open_stream = st;
+  ++S.open_calls;
+  if (S.next % kGroupSlots == 0 || st != nullptr) {  // group full, or not the null stream
+    if (!staging_close(S)) return PLPSH_ERR_HIP;
+    S.next = (S.next + kGroupSlots - 1) / kGroupSlots * kGroupSlots % kSlots;
+  }
   return PLPSH_OK;
 }
 
