@@ -153,7 +153,9 @@ plpsh_status run_bins(int heads, int s, int n, const double* delta, const double
     du[2 * t + 1] = u[t];
   }
   const double* ddu = reinterpret_cast<const double*>(S.dev + slot * S.slot_bytes);
-  if (hip_failed(plpsh::launch_bins(ddu, heads, s, n, bins, st), "bin kernel launch")) return PLPSH_ERR_HIP;
+  if (hip_failed(plpsh::launch_bins(ddu, heads, s, n, bins, plpsh::bins_near_one(delta, hs), st),
+                 "bin kernel launch"))
+    return PLPSH_ERR_HIP;
   S.open_stream = st;
   ++S.open_calls;
   if (S.next % kGroupSlots == 0 || st != nullptr) {  // group full, or not the null stream
@@ -726,6 +728,7 @@ extern "C" plpsh_status plpsh_attention_fwd_noalloc(const void* q, const void* k
 
   // hashes drawn straight into the launch arguments; per-head costs on the way
   double cost[kMaxHeads] = {};
+  bool near_one = false;
   StageArgs a;
   for (int first = 0; first < hs; first += kStagePairs) {
     a.first = first;
@@ -734,11 +737,12 @@ extern "C" plpsh_status plpsh_attention_fwd_noalloc(const void* q, const void* k
       const int h = (first + t) / s, i = (first + t) - h * s;
       plpsh::draw_hash(seed, h, i, sigma[h], &a.du[2 * t], &a.du[2 * t + 1]);
       cost[h] += std::min(a.du[2 * t], static_cast<double>(n));
+      near_one = near_one || plpsh::bins_near_one(&a.du[2 * t], 1);
     }
     hipLaunchKernelGGL(stage_hashes_kernel, dim3(1), dim3(2 * kStagePairs), 0, st, a, du);
     if (hip_failed(hipGetLastError(), "hash staging kernel launch")) return PLPSH_ERR_HIP;
   }
-  if (hip_failed(plpsh::launch_bins(du, heads_q, s, n, bins, st), "bin kernel launch")) return PLPSH_ERR_HIP;
+  if (hip_failed(plpsh::launch_bins(du, heads_q, s, n, bins, near_one, st), "bin kernel launch")) return PLPSH_ERR_HIP;
   uint16_t order[kMaxHeads];
   order_by_cost(heads_q, cost, order);
   if (hip_failed(plpsh::launch_plsh_fwd(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, s, causal, bins,

@@ -9,6 +9,12 @@
 // prefix offsets (the start of every block) by a popcount scan, and writes a
 // 32-byte record per 128-row query tile for the attention kernel.
 //
+// Most hashes take a second kernel with more parallelism: the positions are
+// cut into parts of 8192, one 256-thread workgroup each.  A part needs the
+// number of block starts before it, which has a closed form unless delta is
+// within 2^-30 of 1 (the bound is derived at bins_part_kernel); a launch in
+// which some hash is that close to 1 takes the per-hash kernel.
+//
 // Bit-exactness: every bin value is floor of the IEEE binary64 quotient of
 // the binary64 difference (x - u) by delta, as in the definition; this file
 // is compiled with -ffp-contract=off.  Each position is evaluated (a product
@@ -224,6 +230,152 @@ __global__ __launch_bounds__(kThreads) void bins_kernel(const double* __restrict
   }
 }
 
+// ---- part kernel
+
+constexpr int kPartThreads = 256;
+constexpr int kPartWords = 256;  // 32-position words per part, one per thread; a multiple of 4, so
+                                 // that the four words of a 128-row tile lie in one part
+
+// The bin of x by its definition (binary64 difference, quotient, floor).
+__device__ __forceinline__ double exact_bin(int x, double u, double delta) {
+  return floor((static_cast<double>(x) - u) / delta);
+}
+
+// Smallest x in [0, n] with bin(x) >= k (n if there is none).  Bins never
+// decrease with x; the real-number answer ceil(k delta + u) is taken as the
+// first guess, rounding moves the answer by at most a position or two, and a
+// bisection settles anything further.
+__device__ int first_at_least(double k, double u, double delta, int n) {
+  const double gd = ceil(fma(k, delta, u));
+  int g = gd <= 0.0 ? 0 : (gd >= static_cast<double>(n) ? n : static_cast<int>(gd));
+  for (int it = 0; it < 4; ++it) {
+    if (g > 0 && exact_bin(g - 1, u, delta) >= k) {
+      --g;
+    } else if (g < n && exact_bin(g, u, delta) < k) {
+      ++g;
+    } else {
+      return g;
+    }
+  }
+  int lo = 0, hi = n;  // the answer lies in [lo, hi]
+  while (lo < hi) {
+    const int mid = lo + (hi - lo) / 2;
+    if (exact_bin(mid, u, delta) >= k) hi = mid; else lo = mid + 1;
+  }
+  return lo;
+}
+
+// Exclusive scan of one int per thread over a kPartThreads workgroup.
+__device__ int part_exclusive_scan(int v, int* wsum, int* total) {
+  constexpr int kW = kPartThreads / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int k = 0; k < kW; ++k) {
+    base += k < w ? wsum[k] : 0;
+    tot += wsum[k];
+  }
+  *total = tot;
+  return base + x - v;
+}
+
+// One part (blockIdx.y) of one hash (blockIdx.x).
+//
+// Closed form of the start count.  With n <= 2^19 and u <= delta, the
+// computed difference x - u of consecutive positions is 1 within 2^-32 when
+// delta < 2^19 (larger delta: within 2^-51 delta), and the rounded quotient
+// adds at most 2^-34 / delta each.  So consecutive computed quotients differ
+// by more than 1 when delta <= 1 - 2^-30 (every position starts a block) and
+// by less than 1 when delta >= 1 + 2^-30: bins then rise by 0 or 1 per
+// position, every bin value between bin(0) and bin(n - 1) holds a block, and
+// the starts in [0, x] number bin(x) - bin(0) + 1.
+__global__ __launch_bounds__(kPartThreads) void bins_part_kernel(const double* __restrict__ du, int n, int s,
+                                                                 int ntile, int32_t* __restrict__ nblk,
+                                                                 int32_t* __restrict__ starts,
+                                                                 PlanRec* __restrict__ plan) {
+  __shared__ uint2 wd[kPartWords];  // per word: start bitmap, starts before it within the part
+  __shared__ int wsum[kPartThreads / 64];
+  const int hid = blockIdx.x;
+  const int h = hid / s, i = hid - h * s;
+  const int tid = threadIdx.x;
+  const double delta = du[2 * hid], u = du[2 * hid + 1];
+  const bool every = delta <= 1.0 - 0x1p-30;  // else delta >= 1 + 2^-30 (checked by the launcher)
+  const bool wide = delta >= 32.0;
+  const double rinv = 1.0 / delta;
+  const int nused = (n + 31) >> 5;
+  const int w0 = blockIdx.y * kPartWords;
+  const int w = w0 + tid;
+
+  uint32_t m = 0u;
+  if (w < nused) {
+    const int x0 = 32 * w;
+    m = every ? ~0u : start_flags(x0, u, delta, rinv, wide);
+    if (x0 == 0) m |= 1u;
+    if (n - x0 < 32) m &= (1u << (n - x0)) - 1u;
+  }
+  int total;
+  const int local = part_exclusive_scan(__popc(m), wsum, &total);
+  wd[tid] = make_uint2(m, static_cast<uint32_t>(local));
+
+  // starts before the part, and in all
+  const double b0 = every ? 0.0 : exact_bin(0, u, delta);
+  const int x0p = 32 * w0;
+  const int before = every ? x0p : (x0p == 0 ? 0 : static_cast<int>(exact_bin(x0p - 1, u, delta) - b0) + 1);
+  int32_t* st = starts + static_cast<size_t>(hid) * (n + 1);
+  if (every) {
+    for (int x = x0p + tid; x < min(x0p + 32 * kPartWords, n); x += kPartThreads) st[x] = x;
+  } else {
+    int o = before + local;
+    while (m) {
+      st[o++] = 32 * w + __builtin_ctz(m);
+      m &= m - 1u;
+    }
+  }
+  if (blockIdx.y == gridDim.y - 1 && tid == 0) {
+    const int nb = every ? n : static_cast<int>(exact_bin(n - 1, u, delta) - b0) + 1;
+    nblk[hid] = nb;
+    st[nb] = n;
+  }
+  __syncthreads();
+
+  // plan records of the part's tiles
+  const int q = w0 / 4 + tid;
+  if (tid < kPartWords / 4 && q < ntile) {
+    const int r0 = q * kPlanTile;
+    const int rl = min(r0 + kPlanTile - 1, n - 1);
+    PlanRec rec;
+    if (every) {
+      rec.a = r0;
+      rec.e = r0 + 1;
+      rec.a2 = rl;
+      rec.e2 = rl + 1;
+    } else {
+      const double k0 = exact_bin(r0, u, delta), k1 = exact_bin(rl, u, delta);
+      rec.a = first_at_least(k0, u, delta, n);
+      rec.e = first_at_least(k0 + 1.0, u, delta, n);
+      rec.a2 = first_at_least(k1, u, delta, n);
+      rec.e2 = first_at_least(k1 + 1.0, u, delta, n);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rec.bits[j] = wd[4 * tid + j].x;
+    rec.bits[0] &= ~1u;
+    if (n - r0 < kPlanTile) {
+      const int p = n - r0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rec.bits[j] |= (p >> 5) == j ? 1u << (p & 31) : 0u;
+    }
+    plan[(static_cast<size_t>(h) * ntile + q) * s + i] = rec;
+  }
+}
+
 }  // namespace
 
 BinsLayout bins_layout(int heads, int s, int n) {
@@ -238,10 +390,24 @@ BinsLayout bins_layout(int heads, int s, int n) {
   return L;
 }
 
-hipError_t launch_bins(const double* du, int heads, int s, int n, void* bins, hipStream_t stream) {
+bool bins_near_one(const double* delta, long long count) {
+  for (long long t = 0; t < count; ++t)
+    if (delta[t] > 1.0 - 0x1p-30 && delta[t] < 1.0 + 0x1p-30) return true;
+  return false;
+}
+
+hipError_t launch_bins(const double* du, int heads, int s, int n, void* bins, bool near_one, hipStream_t stream) {
   const BinsLayout L = bins_layout(heads, s, n);
   char* base = static_cast<char*>(bins);
   const int ntile = (n + kPlanTile - 1) / kPlanTile;
+  if (!near_one) {
+    const int parts = (4 * ntile + kPartWords - 1) / kPartWords;
+    hipLaunchKernelGGL(bins_part_kernel, dim3(heads * s, parts), dim3(kPartThreads), 0, stream, du, n, s, ntile,
+                       reinterpret_cast<int32_t*>(base + L.off_nblk),
+                       reinterpret_cast<int32_t*>(base + L.off_starts),
+                       reinterpret_cast<PlanRec*>(base + L.off_plan));
+    return hipGetLastError();
+  }
   const int nwords = 4 * ntile + 4;  // covers positions < 128 (ntile + 1)
   const size_t lds = static_cast<size_t>(nwords) * 2 * sizeof(uint32_t);
   // opt in to the dynamic LDS this launch needs (the largest request so far)

@@ -57,7 +57,9 @@ void draw_hash(uint64_t seed, int h, int i, double sigma, double* delta, double*
 
 // Device launches.  `du` points to heads*s interleaved (delta, u) pairs in
 // device-readable memory.
-hipError_t launch_bins(const double* du, int heads, int s, int n, void* bins, hipStream_t st);
+// near_one: some delta lies within 2^-30 of 1 (such hashes take the per-hash kernel)
+bool bins_near_one(const double* delta, long long count);
+hipError_t launch_bins(const double* du, int heads, int s, int n, void* bins, bool near_one, hipStream_t st);
 
 hipError_t launch_plsh_fwd(const void* q, const void* k, const void* v, void* o,
                            int batch, int hq, int hkv, int n, int d, int dtype,

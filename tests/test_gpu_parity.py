@@ -73,9 +73,19 @@ def _check_bins(bins, delta, u, n, tiles=None):
             assert np.array_equal(got[sel], rec[sel]), (h, i, delta[h, i], u[h, i], n)
 
 
-@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 127, 128, 129, 1000, 4097])
-def test_bins_bit_exact_edge_widths(gpu, n):
-    widths = [0.3, 0.999, 1.0, 1.0 + 2 ** -40, 1.5, 1.999, 2.0, 2.5, 7.3, 64.0, 127.5, 1000.0, float(n), 10.0 * n, 1e9]
+# Widths within 2^-30 of 1 send the whole launch to the per-hash bin kernel;
+# all others take the part kernel, whose start counts have a closed form
+# (every position a start below 1 - 2^-30, bins rising by 0 or 1 above
+# 1 + 2^-30): the widths next to those bounds are here on both sides.
+EDGE_WIDTHS = [0.3, 0.999, 1.0 - 2 ** -29, 1.0 - 2 ** -30, 1.0 + 2 ** -30, 1.0 + 2 ** -29, 1.5, 1.999, 2.0, 2.5,
+               7.3, 64.0, 127.5, 1000.0, 1e9]
+NEAR_ONE_WIDTHS = [1.0, 1.0 + 2 ** -40, 1.0 - 2 ** -40, 1.0 - 2 ** -31, 1.5, 7.3, 0.3, 1000.0]
+
+
+@pytest.mark.parametrize("near_one", [False, True], ids=["part_kernel", "per_hash_kernel"])
+@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 127, 128, 129, 1000, 4097, 8193, 20000])
+def test_bins_bit_exact_edge_widths(gpu, n, near_one):
+    widths = (NEAR_ONE_WIDTHS if near_one else EDGE_WIDTHS) + [float(n), 10.0 * n]
     rng = np.random.default_rng(n)
     delta, u = [], []
     for w in widths:
@@ -85,7 +95,7 @@ def test_bins_bit_exact_edge_widths(gpu, n):
     s = 4
     delta = np.array(delta).reshape(-1, s)
     u = np.array(u).reshape(-1, s)
-    say(f"bins edge widths n={n} hashes={delta.size}")
+    say(f"bins edge widths n={n} near_one={near_one} hashes={delta.size}")
     bins = P.bins_from_hashes(delta, u, n, device=gpu)
     torch.cuda.synchronize()
     _check_bins(bins, delta, u, n)
