@@ -273,21 +273,30 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
       const bool by_a = w == NW - 4;
       int* sk = reinterpret_cast<int*>(sm + SM_SORT) + (by_a ? 0 : 2 * 128);
       int* sv = sk + 128;
+      // the keys go through LDS, whence every lane reads all of them with
+      // broadcast reads, four per read, to count the keys that precede its own
+      // (-e2 is safe: e2 >= 1 for the hashes that take part)
+      int* kst = reinterpret_cast<int*>(sm + SM_KEYS) + (by_a ? 0 : 128);
+      int key[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int i = lane + 64 * x;
+        key[x] = by_a ? static_cast<int>(pr[x][0]) : (i < s ? -static_cast<int>(pr[x][3]) : 0);
+        if ((x == 0 || NCH == 4) && i < s) kst[i] = key[x];
+      }
+      // (the wave's own LDS writes come before its reads: LDS operations of
+      // a wave take effect in order, and the compiler keeps the order)
+      asm volatile("" ::: "memory");
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         if (x == 1 && NCH != 4) break;
         const int i = lane + 64 * x;
-        // (-e2 is safe: e2 >= 1 for the hashes that take part)
-        const int key = by_a ? static_cast<int>(pr[x][0]) : (i < s ? -static_cast<int>(pr[x][3]) : 0);
         int rank = 0;
+        for (int k0 = 0; k0 < s; k0 += 4) {
 #pragma unroll
-        for (int y = 0; y < 2; ++y) {
-          if (y == 1 && NCH != 4) break;
-          const int kend = min(s, 64 * y + 64);
-          const int kv = by_a ? static_cast<int>(pr[y][0]) : (lane + 64 * y < s ? -static_cast<int>(pr[y][3]) : 0);
-          for (int k = 64 * y; k < kend; ++k) {
-            const int kk = __builtin_amdgcn_readlane(kv, k & 63);
-            rank += (kk < key) || (kk == key && k < i);
+          for (int e = 0; e < 4; ++e) {
+            const int k = k0 + e, kv = kst[k];
+            rank += k < s && ((kv < key[x]) || (kv == key[x] && k < i));
           }
         }
         if (i < s) {
@@ -298,26 +307,6 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
           sv[i] = by_a ? INT_MIN : INT_MAX;
         }
       }
-    }
-    // window of keys with weight, and the hashes whose first-row block starts
-    // left of the tile (every wave, from its registers)
-    {
-      int vlo = static_cast<int>(pr[0][0]), vhi = static_cast<int>(pr[0][3]);
-      int vca = static_cast<int>(pr[0][0]) < r0;
-      if constexpr (NCH == 4) {
-        vlo = min(vlo, static_cast<int>(pr[1][0]));
-        vhi = max(vhi, static_cast<int>(pr[1][3]));
-        vca += static_cast<int>(pr[1][0]) < r0;
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        vlo = min(vlo, __shfl_xor(vlo, o, 64));
-        vhi = max(vhi, __shfl_xor(vhi, o, 64));
-        vca += __shfl_xor(vca, o, 64);
-      }
-      lo = __builtin_amdgcn_readfirstlane(vlo);
-      hi = __builtin_amdgcn_readfirstlane(vhi);
-      cntA = __builtin_amdgcn_readfirstlane(vca);
     }
     lds_barrier();
     // H operand through transposing reads of the [position][row] matrix:
@@ -365,6 +354,13 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
       const int* sEa = sAa + 384;
       va0 = sAa[lane];
       if constexpr (NCH == 4) va1 = sAa[64 + lane];
+      // window of keys with weight: from the least block start of the first
+      // row (slot 0 of the a order) to (not causal) the greatest block end of
+      // the last row (slot 0 of the e2 order); and the hashes whose first-row
+      // block starts left of the tile (slots s and above are not hashes)
+      lo = __builtin_amdgcn_readfirstlane(va0);
+      cntA = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < s && va0 < r0));
+      if constexpr (NCH == 4) cntA += __builtin_popcountll(__builtin_amdgcn_ballot_w64(64 + lane < s && va1 < r0));
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
@@ -372,6 +368,7 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
       if constexpr (!CAUSAL) {
         ve0 = sEe[lane];
         if constexpr (NCH == 4) ve1 = sEe[64 + lane];
+        hi = __builtin_amdgcn_readfirstlane(ve0);
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll

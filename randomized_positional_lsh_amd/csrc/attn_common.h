@@ -81,7 +81,8 @@ constexpr int SM_TH = 0;
 constexpr int SM_LO = 256;
 constexpr int SM_HI = SM_LO + 4 * BM;
 constexpr int SM_SORT = SM_HI + 4 * BM;      // 4 x 128 ints: a, e in a order; e2, a2 in e2 order
-constexpr int SMALL = SM_SORT + 4 * 4 * 128;
+constexpr int SM_KEYS = SM_SORT + 4 * 4 * 128;  // 2 x 128 ints: the sort keys (a; -e2)
+constexpr int SMALL = SM_KEYS + 2 * 4 * 128;
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
