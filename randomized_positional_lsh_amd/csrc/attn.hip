@@ -105,8 +105,6 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
   constexpr int SP = 32 * NCH;                 // slots per sorted array
   int va0 = INT_MAX, va1 = INT_MAX;            // a_i sorted (lane k: k-th, k+64-th)
   int ve0 = INT_MIN, ve1 = INT_MIN;            // e2_i sorted descending
-  u32x4 aeL[PL ? NCH : 1][2];                  // e_i of slots 32 ch + 8 g .. + 7 (a order)
-  u32x4 eaL[(PL && !CAUSAL) ? NCH : 1][2];     // a2_i of those slots (e2 order)
   u32x4 pb[2];                                 // boundary bits
   u32x4 pr[2];                                 // a, e, a2, e2
   int lo = 0, hi = n, cntA = 0;
@@ -348,57 +346,18 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
       f.hi_r[rb] = CAUSAL ? min(f.R[rb] + 1, n) : reinterpret_cast<const int*>(sm + SM_HI)[f.rr[rb]];
     }
     {
-      const int* sAa = reinterpret_cast<const int*>(sm + SM_SORT);
-      const int* sAe = sAa + 128;
-      const int* sEe = sAa + 256;
-      const int* sEa = sAa + 384;
-      va0 = sAa[lane];
-      if constexpr (NCH == 4) va1 = sAa[64 + lane];
       // window of keys with weight: from the least block start of the first
       // row (slot 0 of the a order) to (not causal) the greatest block end of
       // the last row (slot 0 of the e2 order); and the hashes whose first-row
       // block starts left of the tile (slots s and above are not hashes)
-      lo = __builtin_amdgcn_readfirstlane(va0);
-      cntA = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < s && va0 < r0));
-      if constexpr (NCH == 4) cntA += __builtin_popcountll(__builtin_amdgcn_ballot_w64(64 + lane < s && va1 < r0));
-#pragma unroll
-      for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-        for (int x = 0; x < 2; ++x) aeL[ch][x] = *reinterpret_cast<const u32x4*>(sAe + 32 * ch + 8 * g + 4 * x);
-      if constexpr (!CAUSAL) {
-        ve0 = sEe[lane];
-        if constexpr (NCH == 4) ve1 = sEe[64 + lane];
-        hi = __builtin_amdgcn_readfirstlane(ve0);
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-          for (int x = 0; x < 2; ++x) eaL[ch][x] = *reinterpret_cast<const u32x4*>(sEa + 32 * ch + 8 * g + 4 * x);
-      }
-    }
-    // far operands: slot k of the a order counts for row r iff r < e_k; slot
-    // k of the e2 order iff r >= a2_k (sentinel slots never count)
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-#pragma unroll
-      for (int ch = 0; ch < NCH; ++ch) {
-        u32x4 fl, fr;
-#pragma unroll
-        for (int u2 = 0; u2 < 4; ++u2) {
-          const int e0 = static_cast<int>(aeL[ch][u2 >> 1][2 * (u2 & 1)]);
-          const int e1 = static_cast<int>(aeL[ch][u2 >> 1][2 * (u2 & 1) + 1]);
-          fl[u2] = (f.R[rb] < e0 ? 0x3F80u : 0u) | (f.R[rb] < e1 ? 0x3F800000u : 0u);
-          if constexpr (!CAUSAL) {
-            const int a0 = static_cast<int>(eaL[ch][u2 >> 1][2 * (u2 & 1)]);
-            const int a1 = static_cast<int>(eaL[ch][u2 >> 1][2 * (u2 & 1) + 1]);
-            fr[u2] = (f.R[rb] >= a0 ? 0x3F80u : 0u) | (f.R[rb] >= a1 ? 0x3F800000u : 0u);
-          }
-        }
-        ufl[rb][ch] = fl;
-        if constexpr (!CAUSAL) ufr[rb][ch] = fr;
-      }
+      const int* sAa = reinterpret_cast<const int*>(sm + SM_SORT);
+      const int a0 = sAa[lane];
+      lo = __builtin_amdgcn_readfirstlane(a0);
+      cntA = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < s && a0 < r0));
+      if constexpr (NCH == 4) cntA += __builtin_popcountll(__builtin_amdgcn_ballot_w64(64 + lane < s && sAa[64 + lane] < r0));
+      if constexpr (!CAUSAL) hi = __builtin_amdgcn_readfirstlane(sAa[256]);  // slot 0 of the e2 order
     }
   }
-
   if constexpr (MODE == MODE_ALIBI) {
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
@@ -530,6 +489,52 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
         f.template chunk<KIND_NEAR, 1>(stage1, stage1 + G::TILE, r0 + BN, r0, n, kc, mkey0, hf);
     }
     t = nnear;
+  }
+  // the sorted orders into registers and the far count operands (after the
+  // near tiles, whose near-count operands they would otherwise sit beside):
+  // slot k of the a order counts for row r iff r < e_k; slot k of the e2
+  // order iff r >= a2_k (sentinel slots never count)
+  if constexpr (PL) {
+    u32x4 aeL[NCH][2];                  // e_i of slots 32 ch + 8 g .. + 7 (a order)
+    u32x4 eaL[CAUSAL ? 1 : NCH][2];     // a2_i of those slots (e2 order)
+    const int* sAa = reinterpret_cast<const int*>(sm + SM_SORT);
+    const int* sAe = sAa + 128;
+    const int* sEe = sAa + 256;
+    const int* sEa = sAa + 384;
+    va0 = sAa[lane];
+    if constexpr (NCH == 4) va1 = sAa[64 + lane];
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+      for (int x = 0; x < 2; ++x) aeL[ch][x] = *reinterpret_cast<const u32x4*>(sAe + 32 * ch + 8 * g + 4 * x);
+    if constexpr (!CAUSAL) {
+      ve0 = sEe[lane];
+      if constexpr (NCH == 4) ve1 = sEe[64 + lane];
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) eaL[ch][x] = *reinterpret_cast<const u32x4*>(sEa + 32 * ch + 8 * g + 4 * x);
+    }
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) {
+        u32x4 fl, fr;
+#pragma unroll
+        for (int u2 = 0; u2 < 4; ++u2) {
+          const int e0 = static_cast<int>(aeL[ch][u2 >> 1][2 * (u2 & 1)]);
+          const int e1 = static_cast<int>(aeL[ch][u2 >> 1][2 * (u2 & 1) + 1]);
+          fl[u2] = (f.R[rb] < e0 ? 0x3F80u : 0u) | (f.R[rb] < e1 ? 0x3F800000u : 0u);
+          if constexpr (!CAUSAL) {
+            const int a0 = static_cast<int>(eaL[ch][u2 >> 1][2 * (u2 & 1)]);
+            const int a1 = static_cast<int>(eaL[ch][u2 >> 1][2 * (u2 & 1) + 1]);
+            fr[u2] = (f.R[rb] >= a0 ? 0x3F80u : 0u) | (f.R[rb] >= a1 ? 0x3F800000u : 0u);
+          }
+        }
+        ufl[rb][ch] = fl;
+        if constexpr (!CAUSAL) ufr[rb][ch] = fr;
+      }
+    }
   }
   {
     u32x4 cb[NRB][4];
