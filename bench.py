@@ -18,7 +18,8 @@ Prints ONE JSON line.  Besides the contract fields it carries:
   roofline     : the attention kernel against the HBM roofline: algorithmic
                  bytes (Q, K, V read once + O written once, per launch)
                  divided by the kernel's median duration with the L2 and the
-                 last-level cache evicted before each launch (the roofline
+                 last-level cache evicted (by a read-only pass over 512 MiB)
+                 before each launch (the roofline
                  figure: a step's inputs are not cache-resident in a model);
                  the back-to-back (warm-cache) figures side by side
   workloads    : tiny, small, qwen3, long: tokens/s of the step, the
@@ -192,16 +193,17 @@ def step_times(run, steps):
 def kernel_times(run, reps, cold):
     """Durations (ms) of the attention kernel alone on the current bins, an
     event pair around each launch on its stream.  cold: a 512 MiB buffer is
-    overwritten on the same stream before every launch, outside the events,
-    which evicts the L2 and the 256 MB last-level cache."""
+    read (summed) on the same stream before every launch, outside the events,
+    which evicts the L2 and the 256 MB last-level cache; the eviction only
+    reads, so no dirty lines of its own are written back during the launch."""
     import torch
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=run.q.device) if cold else None
+    scratch = torch.ones(128 << 20, dtype=torch.float32, device=run.q.device) if cold else None
     for _ in range(3):
         run.attn()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in ev:
         if scratch is not None:
-            scratch.fill_(1)
+            scratch.sum()
         a.record()
         run.attn()
         b.record()

@@ -3,7 +3,12 @@
   python -m randomized_positional_lsh_amd.profsum stats DIR OUT.md --cmd "..."
       Per-kernel rows (calls, mean / min / max duration) of the
       --kernel-trace --stats CSV in DIR for the kernels of this library,
-      labelled by kernel and template instance.
+      labelled by kernel and template instance; and, from the per-dispatch
+      trace, the count-weighted attention kernel's durations at the
+      Mistral shape (--grid: threads per launch, 4096 x 512) split into
+      launches that follow a read-only reduction over a large buffer
+      (bench.py evicts the caches that way before its cold-cache launches)
+      and the others.
 
   python -m randomized_positional_lsh_amd.profsum util DIR OUT.md --cmd "..."
       Unit utilisation of the count-weighted attention kernel from one --pmc
@@ -14,7 +19,8 @@
   python -m randomized_positional_lsh_amd.profsum traffic FETCH WRITE CFETCH CWRITE OUT.json \
           --workload mistral --kernel-sha SHA --copy-bytes N --cmd "..."
       HBM bytes per launch of the count-weighted attention kernel at the
-      Mistral shape (fwd_kernel<128, bf16, causal, 1 hash chunk, mode 0>) from two --pmc runs
+      Mistral shape (fwd_kernel<128, bf16, causal, 1 hash chunk, mode 0>),
+      over its launches that follow the cache-evicting read, from two --pmc runs
       (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), each scaled by the factor
       that makes the same counter read right on plain device copies of
       known total size (CFETCH / CWRITE runs, N bytes read and N written).
@@ -35,6 +41,7 @@ import statistics
 # count-weighted, 1 dense ALiBi, 2 one short attention per hash; the backward
 # template's <head_dim, causal, hash chunks, keys side>.
 MAIN = "fwd_kernel<128, true, true, 1, 0>"
+EVICT = "reduce_kernel"  # torch's reduction kernel: bench.py's read-only cache eviction
 _MODES = {"0": "attention, count-weighted", "1": "dense exact ALiBi", "2": "one attention per hash"}
 _PLAIN = [
     ("bins_kernel", "bin boundaries"),
@@ -71,7 +78,7 @@ def _short(name: str) -> str | None:
     return None
 
 
-def stats(d: str, out: str, cmd: str) -> None:
+def stats(d: str, out: str, cmd: str, grid: int = 4096 * 512) -> None:
     path = _one(os.path.join(d, "**", "*kernel_stats.csv"))
     rows = list(csv.DictReader(open(path)))
     lines = ["# Kernel trace summary", "", f"Command: `{cmd}`", "",
@@ -84,6 +91,24 @@ def stats(d: str, out: str, cmd: str) -> None:
         lines.append(f"| {s} | {r['Calls']} | {float(r['AverageNs']) * ns:.2f} | {float(r['MinNs']) * ns:.2f} | "
                      f"{float(r['MaxNs']) * ns:.2f} | {float(r['Percentage']):.1f}% |")
     lines += ["", f"Source: {os.path.basename(path)} (rocprofv3 --kernel-trace --stats --output-format csv)."]
+    traces = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if traces:
+        seq = sorted(csv.DictReader(open(traces[0])), key=lambda r: int(r["Start_Timestamp"]))
+        cold, warm = [], []
+        for prev, r in zip([None] + seq[:-1], seq):
+            if MAIN not in r["Kernel_Name"] or int(r["Grid_Size_X"]) != grid:
+                continue
+            us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+            (cold if prev is not None and EVICT in prev["Kernel_Name"] else warm).append(us)
+        if cold or warm:
+            lines += ["", f"Count-weighted attention ({MAIN}), launches of {grid // 512} workgroups (the "
+                      "Mistral-shaped layer), per dispatch (kernel trace, us):", "",
+                      "| launches | calls | median | mean | p10 | p90 |", "|---|---|---|---|---|---|"]
+            for name, x in (("after a cache-evicting read (cold)", cold), ("others (warm)", warm)):
+                if x:
+                    q = statistics.quantiles(x, n=10) if len(x) > 1 else [x[0]] * 9
+                    lines.append(f"| {name} | {len(x)} | {statistics.median(x):.2f} | {statistics.mean(x):.2f} | "
+                                 f"{q[0]:.2f} | {q[-1]:.2f} |")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -119,12 +144,19 @@ def util(d: str, out: str, cmd: str, cus: int = 256, simds: int = 1024, xcds: in
     print("\n".join(lines))
 
 
-def _counter_kib(d: str, regex_part: str, counter: str) -> list[float]:
+def _counter_kib(d: str, regex_part: str, counter: str, cold_only: bool = False) -> list[float]:
+    """Per-dispatch sums of `counter` for kernels matching `regex_part`;
+    cold_only: only dispatches that directly follow the cache-evicting read."""
     path = _one(os.path.join(d, "**", "*counter_collection.csv"))
-    per = {}
+    per, names = {}, {}
     for r in csv.DictReader(open(path)):
+        names[int(r["Dispatch_Id"])] = r["Kernel_Name"]
         if regex_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
-            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+            per[int(r["Dispatch_Id"])] = per.get(int(r["Dispatch_Id"]), 0.0) + float(r["Counter_Value"])
+    if cold_only:
+        ids = sorted(names)
+        prev = {b: a for a, b in zip(ids, ids[1:])}
+        per = {k: v for k, v in per.items() if k in prev and EVICT in names[prev[k]]}
     if not per:
         raise ValueError(f"no {counter} rows for kernels matching {regex_part!r} in {path}")
     return list(per.values())
@@ -132,8 +164,8 @@ def _counter_kib(d: str, regex_part: str, counter: str) -> list[float]:
 
 def traffic(fetch: str, write: str, cfetch: str, cwrite: str, out: str, workload: str, sha: str,
             copy_bytes: int, cmd: str) -> None:
-    f = _counter_kib(fetch, MAIN, "FETCH_SIZE")
-    w = _counter_kib(write, MAIN, "WRITE_SIZE")
+    f = _counter_kib(fetch, MAIN, "FETCH_SIZE", cold_only=True)
+    w = _counter_kib(write, MAIN, "WRITE_SIZE", cold_only=True)
     cf = sum(_counter_kib(cfetch, "copyBuffer", "FETCH_SIZE")) * 1024.0
     cw = sum(_counter_kib(cwrite, "copyBuffer", "WRITE_SIZE")) * 1024.0
     sf, sw = copy_bytes / cf, copy_bytes / cw
@@ -142,7 +174,8 @@ def traffic(fetch: str, write: str, cfetch: str, cwrite: str, out: str, workload
     res = {"kernel_sha": sha, "workload": workload, "bytes_per_launch": int(round(fb + wb)),
            "fetch_bytes": int(round(fb)), "write_bytes": int(round(wb)),
            "fetch_scale": round(sf, 5), "write_scale": round(sw, 5),
-           "dispatches": {"fetch": len(f), "write": len(w)}, "command": cmd}
+           "dispatches": {"fetch": len(f), "write": len(w)}, "launches": "after a cache-evicting read",
+           "command": cmd}
     with open(out, "w") as fo:
         json.dump(res, fo, indent=1)
         fo.write("\n")
@@ -156,6 +189,7 @@ def main() -> None:
     a.add_argument("dir")
     a.add_argument("out")
     a.add_argument("--cmd", required=True)
+    a.add_argument("--grid", type=int, default=4096 * 512)
     c = sub.add_parser("util")
     c.add_argument("dir")
     c.add_argument("out")
@@ -169,7 +203,7 @@ def main() -> None:
     b.add_argument("--cmd", required=True)
     args = ap.parse_args()
     if args.cmd_name == "stats":
-        stats(args.dir, args.out, args.cmd)
+        stats(args.dir, args.out, args.cmd, args.grid)
     elif args.cmd_name == "util":
         util(args.dir, args.out, args.cmd)
     else:
