@@ -74,10 +74,24 @@ __device__ __forceinline__ uint32_t start_flags(int x0, double u, double delta, 
       if (ok) return 1u << hi;
     }
   }
+  // The 33 bins from one product and then one fused multiply-add each:
+  // q_k = k rinv + q_0 lies within 36 2^-53 max(|q_0|, |q_k|, 32 / delta) of
+  // the exact quotient (q_0's three roundings, k times the reciprocal's, the
+  // fma's own), and the binary64 quotient of the definition within 2^-52 |q|
+  // of it, so a fractional part farther than 2^-47 max(|q_0|, |q_32|,
+  // 32 rinv) from an integer settles the floor.
+  const double q0 = (static_cast<double>(x0 - 1) - u) * rinv;
+  const double margin = 0x1p-47 * fmax(fmax(fabs(q0), fabs(fma(32.0, rinv, q0))), 32.0 * rinv);
   double f[33];
   bool exact = false;
 #pragma unroll
-  for (int k = 0; k < 33; ++k) exact = !certified_bin(x0 - 1 + k, u, rinv, &f[k]) || exact;
+  for (int k = 0; k < 33; ++k) {
+    const double q = fma(static_cast<double>(k), rinv, q0);
+    const double fl = floor(q);
+    const double fr = q - fl;  // exact for |q| < 2^52
+    f[k] = fl;
+    exact = exact || !(fr > margin && fr < 1.0 - margin);
+  }
   uint32_t m = 0u;
   if (!exact) {
 #pragma unroll
