@@ -80,7 +80,7 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
   f.g = f.lane >> 4;
   f.w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = f.lane, l16 = f.l16, g = f.g, w = f.w;
-  f.sTh = sm + SM_TH;
+  f.sTh = lds_addr(sm + SM_TH);
 
   // ---- work item: consecutive tiles of a head stay on one XCD
   const int gid = blockIdx.x;

@@ -220,8 +220,9 @@ struct Fwd {
   int koff[BF ? 1 : KS / 4];   // fp32: logit-operand chunk offsets within a row block
   uint32_t kbase;              // bf16: logit-operand offset of k-step 0; k-step ks: ^ 64 ks
   uint32_t ka[BF ? KS : 1];    // bf16: LDS addresses of the current tile's logit operand, per k-step
+  uint32_t vbase;              // bf16: LDS address of the current tile's value operand (this lane, block 0)
   int vtr0;                    // value-operand (transposing read) offset of block 0; block db: ^ 32 db
-  const unsigned char* sTh;
+  uint32_t sTh;                // LDS address of the table of bf16 prefixes of ones
 
   __device__ __forceinline__ void init_offsets() {
     // K operand: key = 16 kb + l16; logical chunk c = 4 ks + g (bf16) or (KS/4) g + c4 (fp32)
@@ -254,6 +255,7 @@ struct Fwd {
       const uint32_t b = lds_addr(sK) + kbase;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) ka[ks] = b ^ (64 * ks);
+      vbase = lds_addr(sK + G::TILE) + vtr0;
     }
   }
 
@@ -308,7 +310,7 @@ struct Fwd {
           // c[r, j] = nbase[r][ch] + sum over positions p of chunk ch with p <= j of H[r, p]
           const int jrel0 = 64 * TI + 16 * kb;
           const int ch = jrel0 >> 5;
-          const u32x4 th = lds128(sTh + 16 * clamp08(jrel0 + l16 - 32 * ch - 8 * g + 1));
+          const u32x4 th = lds128_at(sTh + 16 * clamp08(jrel0 + l16 - 32 * ch - 8 * g + 1));
 #pragma unroll
           for (int rb = 0; rb < NRB; ++rb) {
             const float b0 = nbase[rb][ch];
@@ -317,7 +319,7 @@ struct Fwd {
         } else {
 #pragma unroll
           for (int ch = 0; ch < NCH; ++ch) {
-            const u32x4 th = lds128(sTh + 16 * clamp08(mkey[kb] - 32 * ch - 8 * g));
+            const u32x4 th = lds128_at(sTh + 16 * clamp08(mkey[kb] - 32 * ch - 8 * g));
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) cacc[kb2][rb] = mfma_bf16(th, cnt_b[rb][ch], cacc[kb2][rb]);
           }
@@ -404,10 +406,12 @@ struct Fwd {
         pf[rb] = u32x4{pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]), pack_bf16(p[1][0], p[1][1]),
                        pack_bf16(p[1][2], p[1][3])};
       }
-      const unsigned char* vb = sV + (32 * kc) * G::RB;
+      (void)sV;  // (its LDS address is vbase, set by begin_k)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const uint32_t va = (lds_addr(vb) + vtr0) ^ (32 * db);
+        // key offsets 32 kc RB are multiples of 256, so adding them commutes
+        // with the block XOR
+        const uint32_t va = (vbase + (32 * kc) * G::RB) ^ (32 * db);
         const u32x2 v0 = lds_tr16_at(va);
         const u32x2 v1 = lds_tr16_at(va + 16 * G::RB);
         const u32x4 a = {v0[0], v0[1], v1[0], v1[1]};
