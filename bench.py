@@ -1,10 +1,11 @@
 #!/usr/bin/env python3
 """Throughput of Positional-LSH ALiBi attention on one MI355X.
 
-A step is one pass of the whole path over one batch of resident inputs:
-host draw of the s hashes per head, the device bin kernel, and the fused
-attention kernel (plpsh_sample_bins + plpsh_attention_fwd_bins, i.e. what
-plpsh_attention_fwd does).  Default workload: one Mistral-7B-shaped
+A step is one pass of the whole path over one batch of resident inputs,
+one plpsh_attention_fwd call: host draw of the s hashes per head, then one
+kernel that evaluates the bins of each query tile, writes the bin buffer
+(block counts, block starts, plan records) and computes the count-weighted
+attention.  Default workload: one Mistral-7B-shaped
 attention layer (batch 1, 32 query / 8 KV heads, n = 16384, head_dim 128,
 bf16, causal, s = 20, sigma_h = 2^(8(h+1)/32)), synthetic N(0, 1) inputs.
 
@@ -17,6 +18,8 @@ duration (an event pair around each launch, on the stream it runs on).
 Prints ONE JSON line.  Besides the contract fields it carries:
   step_ms      : median, p10, p90 of the step time (separate pass: 20
                  groups of 5 steps, an event at each group boundary)
+  two_launch   : the same step as two launches (plpsh_sample_bins, whose
+                 bin kernel writes the buffer, then plpsh_attention_fwd_bins)
   roofline     : the attention kernel against the HBM roofline: algorithmic
                  bytes (Q, K, V read once + O written once, per launch)
                  divided by the kernel's median duration with the L2 and the
@@ -134,6 +137,20 @@ class Runner:
         self.nws = self.ws.numel()
         self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
+    def step(self):
+        """The whole path in one call (one kernel launch)."""
+        W = self.W
+        st = self.lib.plpsh_attention_fwd(*self.vp, W.batch, W.heads_q, W.heads_kv, W.n, W.head_dim, self.dtype,
+                                          self.p_sig, W.s, ctypes.c_uint64(W.hash_seed), int(W.causal), self.p_ws,
+                                          self.nws, self.stream)
+        if st:
+            raise RuntimeError(self.P.status_string(st))
+
+    def two_launch(self):
+        """The same step as the bin kernel, then attention on its buffer."""
+        self.bins()
+        self.attn()
+
     def bins(self):
         W = self.W
         st = self.lib.plpsh_sample_bins(W.hash_seed, W.heads_q, W.s, W.n, self.p_sig, self.p_delta, self.p_u,
@@ -162,13 +179,11 @@ def time_steps(run, steps, warmup):
     the stream in between)."""
     import torch
     for _ in range(warmup):
-        run.bins()
-        run.attn()
+        run.step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        run.bins()
-        run.attn()
+        run.step()
     torch.cuda.synchronize()
     return time.perf_counter() - t0
 
@@ -188,29 +203,29 @@ def step_times(run, groups, per=5):
     ev[0].record()
     for i in range(groups):
         for _ in range(per):
-            run.bins()
-            run.attn()
+            run.step()
         ev[i + 1].record()
     torch.cuda.synchronize()
     return [ev[i].elapsed_time(ev[i + 1]) / per for i in range(groups)]
 
 
 def kernel_times(run, reps, cold):
-    """Durations (ms) of the attention kernel alone on the current bins, an
-    event pair around each launch on its stream.  cold: a 512 MiB buffer is
+    """Durations (ms) of the step's kernel, an event pair around each launch
+    on its stream (the host draws the hashes while the GPU still runs the
+    work enqueued before, so the pair spans the kernel).  cold: a 512 MiB buffer is
     read (summed) on the same stream before every launch, outside the events,
     which evicts the L2 and the 256 MB last-level cache; the eviction only
     reads, so no dirty lines of its own are written back during the launch."""
     import torch
     scratch = torch.ones(128 << 20, dtype=torch.float32, device=run.q.device) if cold else None
     for _ in range(3):
-        run.attn()
+        run.step()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in ev:
         if scratch is not None:
             scratch.sum()
         a.record()
-        run.attn()
+        run.step()
         b.record()
     torch.cuda.synchronize()
     del scratch
@@ -551,20 +566,29 @@ def main():
     # loop that follows starts on a GPU at its steady clocks with the
     # buffers' pages mapped, whatever its own warmup count
     for _ in range(50):  # the device's clocks ramp up under the first milliseconds of load
-        run.bins()
-        run.attn()
+        run.step()
     steps_ms = step_times(run, 20)
     warm = kernel_times(run, 50, cold=False)
     cold = kernel_times(run, 50, cold=True)
     wall = time_steps(run, args.steps, args.warmup)
     ms_step = 1e3 * wall / args.steps
     tokens = W.batch * W.n
+    # the two-launch form of the same step, for reference; it also leaves the
+    # host copy of this draw in run.delta / run.u for the legs below
+    for _ in range(20):
+        run.two_launch()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(100):
+        run.two_launch()
+    torch.cuda.synchronize()
+    ms_two = 1e3 * (time.perf_counter() - t0) / 100
     value = tokens / (wall / args.steps)
     log(f"step {ms_step:.4f} ms ({args.steps} timed steps after {args.warmup} warmup steps)")
     kern_ms = float(np.median(cold))
     warm_ms = float(np.median(warm))
-    log(f"step median {np.median(steps_ms):.4f} ms; attention kernel median {kern_ms:.4f} ms with caches evicted, "
-        f"{warm_ms:.4f} ms back to back")
+    log(f"step median {np.median(steps_ms):.4f} ms; kernel median {kern_ms:.4f} ms with caches evicted, "
+        f"{warm_ms:.4f} ms back to back; two-launch step {ms_two:.4f} ms")
 
     delta = run.delta.reshape(W.heads_q, W.s).copy()
     u = run.u.reshape(W.heads_q, W.s).copy()
@@ -580,7 +604,8 @@ def main():
     tflops = flops / (kern_ms * 1e-3) / 1e12
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "plpsh fwd_kernel (attention)", "cache": "L2 and last-level cache evicted before each launch",
+                "kernel": "plpsh fwd_kernel (bins of each query tile + attention)",
+                "cache": "L2 and last-level cache evicted before each launch",
                 "kernel_ms": round(kern_ms, 5), "kernel_ms_pct": pct(cold), "algorithmic_bytes": abytes,
                 "useful_tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                 "kernel_ms_warm": round(warm_ms, 5), "kernel_ms_warm_pct": pct(warm),
@@ -595,6 +620,7 @@ def main():
                    "n": W.n, "head_dim": W.head_dim, "s": W.s, "causal": W.causal,
                    "sigma": "2^(8(h+1)/H)", "parallelism": "single GPU"},
         "step_ms": pct(steps_ms),
+        "two_launch": {"step_ms": round(ms_two, 5), "tokens_per_s": round(tokens / (ms_two * 1e-3), 1)},
         "roofline": roofline,
     }
     if W.dtype == "bf16" and not args.no_backward:

@@ -136,9 +136,11 @@ bool valid_hs(int heads, int s) {
          static_cast<long long>(heads) * s <= PLPSH_MAX_HASHES;
 }
 
-// Upload (delta, u) into a pinned slot and launch the bin kernel on it.
-plpsh_status run_bins(int heads, int s, int n, const double* delta, const double* u, void* bins,
-                      hipStream_t st) {
+// Upload (delta, u) into a pinned slot and launch(device address of the
+// pairs), the one kernel that reads them.
+template <class Launch>
+plpsh_status with_staged_hashes(int heads, int s, const double* delta, const double* u, hipStream_t st,
+                                const char* what, Launch&& launch) {
   int dev = 0;
   if (hip_failed(hipGetDevice(&dev), "hipGetDevice")) return PLPSH_ERR_HIP;
   if (dev < 0 || dev >= kMaxDevices) return PLPSH_ERR_UNSUPPORTED;
@@ -153,9 +155,7 @@ plpsh_status run_bins(int heads, int s, int n, const double* delta, const double
     du[2 * t + 1] = u[t];
   }
   const double* ddu = reinterpret_cast<const double*>(S.dev + slot * S.slot_bytes);
-  if (hip_failed(plpsh::launch_bins(ddu, heads, s, n, bins, plpsh::bins_near_one(delta, hs), st),
-                 "bin kernel launch"))
-    return PLPSH_ERR_HIP;
+  if (hip_failed(launch(ddu), what)) return PLPSH_ERR_HIP;
   S.open_stream = st;
   ++S.open_calls;
   if (S.next % kGroupSlots == 0 || st != nullptr) {  // group full, or not the null stream
@@ -163,6 +163,15 @@ plpsh_status run_bins(int heads, int s, int n, const double* delta, const double
     S.next = (S.next + kGroupSlots - 1) / kGroupSlots * kGroupSlots % kSlots;
   }
   return PLPSH_OK;
+}
+
+// The bin kernel on staged hashes.
+plpsh_status run_bins(int heads, int s, int n, const double* delta, const double* u, void* bins,
+                      hipStream_t st) {
+  const bool near_one = plpsh::bins_near_one(delta, static_cast<long long>(heads) * s);
+  return with_staged_hashes(heads, s, delta, u, st, "bin kernel launch", [&](const double* ddu) {
+    return plpsh::launch_bins(ddu, heads, s, n, bins, near_one, st);
+  });
 }
 
 // Common argument checks of the attention entry points (everything except
@@ -194,12 +203,9 @@ void order_by_cost(int hq, const double* cost, uint16_t* order) {
   std::sort(order, order + hq, [&](uint16_t a, uint16_t b) { return cost[a] > cost[b] || (cost[a] == cost[b] && a < b); });
 }
 
-// Launch the attention kernel on a computed bin buffer.  Heads with the
-// widest bins (largest key windows) are scheduled first when delta is known.
-plpsh_status attention_on_bins(const void* q, const void* k, const void* v, void* o, int batch, int hq, int hkv,
-                               int n, int d, int dtype, const double* delta, int s, int causal, const void* bins,
-                               hipStream_t st, bool literal = false, float* lse = nullptr) {
-  uint16_t order[kMaxHeads];
+// Heads with the widest bins (largest key windows) first when delta is
+// known, else the natural order.
+void head_order(int hq, int s, int n, const double* delta, uint16_t* order) {
   double cost[kMaxHeads];
   for (int h = 0; h < hq; ++h) {
     cost[h] = 0.0;
@@ -207,6 +213,14 @@ plpsh_status attention_on_bins(const void* q, const void* k, const void* v, void
       for (int i = 0; i < s; ++i) cost[h] += std::min(delta[h * s + i], static_cast<double>(n));
   }
   order_by_cost(hq, cost, order);
+}
+
+// Launch the attention kernel on a computed bin buffer.
+plpsh_status attention_on_bins(const void* q, const void* k, const void* v, void* o, int batch, int hq, int hkv,
+                               int n, int d, int dtype, const double* delta, int s, int causal, const void* bins,
+                               hipStream_t st, bool literal = false, float* lse = nullptr) {
+  uint16_t order[kMaxHeads];
+  head_order(hq, s, n, delta, order);
   if (hip_failed(plpsh::launch_plsh_fwd(q, k, v, o, batch, hq, hkv, n, d, dtype, s, causal, bins, order, literal,
                                         lse, st),
                  "attention kernel launch"))
@@ -219,9 +233,20 @@ plpsh_status attention_common(const void* q, const void* k, const void* v, void*
                               void* ws, void* stream) {
   if (batch == 0 || n == 0) return PLPSH_OK;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  plpsh_status r = run_bins(hq, s, n, delta, u, ws, st);
-  if (r != PLPSH_OK) return r;
-  return attention_on_bins(q, k, v, o, batch, hq, hkv, n, d, dtype, delta, s, causal, ws, st);
+  if (plpsh::bins_near_one(delta, static_cast<long long>(hq) * s)) {
+    // some start count without a closed form: the per-hash bin kernel first
+    plpsh_status r = run_bins(hq, s, n, delta, u, ws, st);
+    if (r != PLPSH_OK) return r;
+    return attention_on_bins(q, k, v, o, batch, hq, hkv, n, d, dtype, delta, s, causal, ws, st);
+  }
+  // one launch: the attention kernel evaluates the bins of its query tiles
+  // and writes the bin buffer as the bin kernel would
+  uint16_t order[kMaxHeads];
+  head_order(hq, s, n, delta, order);
+  return with_staged_hashes(hq, s, delta, u, st, "attention kernel launch", [&](const double* ddu) {
+    return plpsh::launch_plsh_fwd(q, k, v, o, batch, hq, hkv, n, d, dtype, s, causal, ws, order, false, nullptr,
+                                  st, ddu);
+  });
 }
 
 // ---- error of the mask mean against L* (Theorem 2.1), large n
@@ -742,11 +767,14 @@ extern "C" plpsh_status plpsh_attention_fwd_noalloc(const void* q, const void* k
     hipLaunchKernelGGL(stage_hashes_kernel, dim3(1), dim3(2 * kStagePairs), 0, st, a, du);
     if (hip_failed(hipGetLastError(), "hash staging kernel launch")) return PLPSH_ERR_HIP;
   }
-  if (hip_failed(plpsh::launch_bins(du, heads_q, s, n, bins, near_one, st), "bin kernel launch")) return PLPSH_ERR_HIP;
+  // with every start count in closed form the attention kernel evaluates its
+  // own plan (one launch), else the per-hash bin kernel runs first
+  if (near_one && hip_failed(plpsh::launch_bins(du, heads_q, s, n, bins, true, st), "bin kernel launch"))
+    return PLPSH_ERR_HIP;
   uint16_t order[kMaxHeads];
   order_by_cost(heads_q, cost, order);
   if (hip_failed(plpsh::launch_plsh_fwd(q, k, v, o, batch, heads_q, heads_kv, n, head_dim, dtype, s, causal, bins,
-                                        order, false, nullptr, st),
+                                        order, false, nullptr, st, near_one ? nullptr : du),
                  "attention kernel launch"))
     return PLPSH_ERR_HIP;
   return PLPSH_OK;

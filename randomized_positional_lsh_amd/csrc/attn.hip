@@ -51,9 +51,96 @@
 // MODE_ALIBI computes exact dense ALiBi attention, weight e^{S - |r-j|/sigma},
 // over every key with the same pipeline.
 #include "attn_common.h"
+#include "bins_device.h"
 
 namespace plpsh {
 namespace {
+
+// Plan records of query tile r0 .. r0 + 127 for the hashes of head h,
+// evaluated from (delta, u) (bins_device.h): the record of hash i goes to
+// srec + 32 i, in the layout of PlanRec, and the block index of row r0's
+// block, bin(r0) - bin(0) (r0 when every position starts a block), to
+// sbase[i].  Waves 0-3 take the start flags of the tile's 32-position words
+// 0-3, waves 4-7 the block bounds a, e (block of row r0) and a2, e2 (block
+// of the last row); lane l takes hashes l and l + 64.  In the last tile the
+// workgroup of batch row 0 writes the block count and the closing entry n
+// of the bin buffer (scatter_starts below writes the starts).  The launcher
+// sends no delta within 2^-30 of 1 here (there the start count has no
+// closed form).
+template <bool CAUSAL, int NCH>
+__device__ __forceinline__ void plan_tile(const FwdArgs& A, const double (&hd)[2], const double (&hu)[2], int h,
+                                          int b, int qt, int r0, int n, int s, int w, int lane,
+                                          unsigned char* srec, int* sbase) {
+  const int rl = min(r0 + BM - 1, n - 1);
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    if (x == 1 && NCH != 4) break;
+    const int i = lane + 64 * x;
+    if (i >= s) continue;
+    const double delta = hd[x], u = hu[x];
+    const bool every = delta <= 1.0 - 0x1p-30;
+    const double rinv = 1.0 / delta;
+    uint32_t* rec = reinterpret_cast<uint32_t*>(srec + 32 * i);
+    if (w < 4) {
+      const int x0 = r0 + 32 * w;
+      uint32_t m = 0u;
+      if (x0 < n) {
+        double prev;
+        m = every ? ~0u : start_flags(x0, u, delta, rinv, delta >= 32.0, &prev);
+        if (n - x0 < 32) m &= (1u << (n - x0)) - 1u;
+      }
+      // bit p: position r0 + p (1 <= p < 128) starts a block, or equals n
+      if (w == 0) m &= ~1u;
+      const int p = n - r0;
+      if (p < BM && (p >> 5) == w) m |= 1u << (p & 31);
+      rec[4 + w] = m;
+    } else {
+      const int j = w - 4;
+      const int r = j < 2 ? r0 : rl;
+      const double kr = every ? 0.0 : bin_at(r, u, delta, rinv);
+      const int val = every ? r + (j & 1) : first_at_least(kr + static_cast<double>(j & 1), u, delta, rinv, n);
+      rec[j] = static_cast<uint32_t>(val);
+      if (j == 1) sbase[i] = every ? r0 : static_cast<int>(kr - exact_bin(0, u, delta));
+      if (j == 3 && b == 0 && A.starts != nullptr && qt == A.ntile - 1) {
+        const int nb = every ? n : static_cast<int>(exact_bin(n - 1, u, delta) - exact_bin(0, u, delta)) + 1;
+        A.nblk[h * s + i] = nb;
+        A.starts[static_cast<size_t>(h * s + i) * (n + 1) + nb] = n;
+      }
+    }
+  }
+}
+
+// The block starts that lie in query tile r0 .. r0 + 127, at their block
+// indices in the bin buffer, from the records plan_tile left in LDS: bins
+// rise by one at each start, so the tile's starts take consecutive indices,
+// the first one that of row r0's block if it starts at r0, else the next.
+// Waves 0-3 take words 0-3 of the tile, lane l hashes l and l + 64.
+template <int NCH>
+__device__ __forceinline__ void scatter_starts(const FwdArgs& A, int h, int r0, int n, int s, int w, int lane,
+                                               const unsigned char* srec, const int* sbase) {
+  if (w >= 4) return;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    if (x == 1 && NCH != 4) break;
+    const int i = lane + 64 * x;
+    if (i >= s) continue;
+    const uint32_t* rec = reinterpret_cast<const uint32_t*>(srec + 32 * i);
+    const int p = n - r0;  // the closing bit (position n), not a start
+    const bool r0s = static_cast<int>(rec[0]) == r0;  // row r0's block starts at r0
+    int o = sbase[i] + (r0s ? 0 : 1);
+    uint32_t m = 0u;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      uint32_t bv = rec[4 + v];
+      if (p < BM && (p >> 5) == v) bv &= ~(1u << (p & 31));
+      if (v == 0 && r0s) bv |= 1u;
+      if (v < w) o += __builtin_popcount(bv);
+      if (v == w) m = bv;
+    }
+    int32_t* st = A.starts + static_cast<size_t>(h * s + i) * (n + 1);
+    for (; m != 0u; m &= m - 1u) st[o++] = r0 + 32 * w + __builtin_ctz(m);
+  }
+}
 
 template <int D, bool BF, bool CAUSAL, int NCH, int MODE>
 // second bound: waves per SIMD, from the workgroups that fit a CU's LDS
@@ -108,7 +195,19 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
   u32x4 pb[2];                                 // boundary bits
   u32x4 pr[2];                                 // a, e, a2, e2
   int lo = 0, hi = n, cntA = 0;
-  if constexpr (PL || LIT) {
+  // in-kernel plan: (delta, u) of hashes lane and lane + 64, else plan records
+  const bool inplan = PL && A.du != nullptr;
+  double hd[2] = {1.0, 1.0}, hu[2] = {0.0, 0.0};
+  if (inplan) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int i = lane + 64 * x;
+      const bool ok = (x == 0 || NCH == 4) && i < s;
+      const double* p = A.du + 2 * (static_cast<size_t>(h) * s + (i < s ? i : 0));
+      hd[x] = ok ? p[0] : 1.0;
+      hu[x] = ok ? p[1] : 0.0;
+    }
+  } else if constexpr (PL || LIT) {
     const size_t tix = static_cast<size_t>(h) * A.ntile + qt;
     const PlanRec* rec = A.plan + tix * s;
 #pragma unroll
@@ -181,7 +280,29 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
       reinterpret_cast<int*>(sm + SM_LO)[tid] = INT_MAX;
       reinterpret_cast<int*>(sm + SM_HI)[tid] = INT_MIN;
     }
+    if (inplan) plan_tile<CAUSAL, NCH>(A, hd, hu, h, b, qt, r0, n, s, w, lane, sm + SM_REC,
+                                        reinterpret_cast<int*>(sm + SM_BASE));
     lds_barrier();
+    if (inplan) {
+      const bool out = b == 0 && A.plan_out != nullptr;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int i = lane + 64 * x;
+        const bool ok = (x == 0 || NCH == 4) && i < s;
+        const u32x4* rec = reinterpret_cast<const u32x4*>(sm + SM_REC + 32 * (i & 127));
+        const u32x4 ae = rec[0], bits = rec[1];
+        pb[x] = ok ? bits : u32x4{0, 0, 0, 0};
+        // causal rows never see the last row's block (a2, e2): sentinels, as
+        // when the records are loaded
+        pr[x] = ok ? (CAUSAL ? u32x4{ae[0], ae[1], 0x7FFFFFFFu, 0x80000000u} : ae)
+                   : u32x4{0x7FFFFFFFu, 0x80000000u, 0x7FFFFFFFu, 0x80000000u};
+        if (w == 0 && out && ok) {
+          PlanRec* po = A.plan_out + (static_cast<size_t>(h) * A.ntile + qt) * s + i;
+          reinterpret_cast<u32x4*>(po)[0] = ae;
+          reinterpret_cast<u32x4*>(po)[1] = bits;
+        }
+      }
+    }
     ld.issue(Kh, Vh, r0, n, stage0, w);
     {
       // H[r][p] (stored [p][r], biased int16) by atomic adds: wave w takes the
@@ -623,6 +744,12 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
       }
     }
   }
+  // the tile's block starts in the bin buffer (in-kernel plan, batch row 0),
+  // off the set-up's path
+  if constexpr (PL) {
+    if (inplan && b == 0 && A.starts != nullptr)
+      scatter_starts<NCH>(A, h, r0, n, s, w, lane, sm + SM_REC, reinterpret_cast<const int*>(sm + SM_BASE));
+  }
 }
 
 template <int D, bool BF, bool CAUSAL, int NCH, int MODE>
@@ -675,12 +802,18 @@ int grid_size(int ntile, int instances, int* cs) {
 
 hipError_t launch_plsh_fwd(const void* q, const void* k, const void* v, void* o, int batch, int hq, int hkv,
                            int n, int d, int dtype, int s, int causal, const void* bins, const uint16_t* order,
-                           bool literal, float* lse, hipStream_t st) {
+                           bool literal, float* lse, hipStream_t st, const double* du) {
   const BinsLayout L = bins_layout(hq, s, n);
+  char* base = const_cast<char*>(static_cast<const char*>(bins));
   FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.lse = lse;
-  a.plan = reinterpret_cast<const PlanRec*>(static_cast<const char*>(bins) + L.off_plan);
+  a.plan = reinterpret_cast<const PlanRec*>(base + L.off_plan);
+  const bool inplan = du != nullptr && !literal;
+  a.du = inplan ? du : nullptr;
+  a.nblk = inplan ? reinterpret_cast<int32_t*>(base + L.off_nblk) : nullptr;
+  a.starts = inplan ? reinterpret_cast<int32_t*>(base + L.off_starts) : nullptr;
+  a.plan_out = inplan ? reinterpret_cast<PlanRec*>(base + L.off_plan) : nullptr;
   a.B = batch; a.Hq = hq; a.Hkv = hkv; a.n = n; a.s = s;
   a.ntile = (n + BM - 1) / BM;
   const int grid = grid_size(a.ntile, batch * hq, &a.cs);
@@ -697,6 +830,10 @@ hipError_t launch_alibi_fwd(const void* q, const void* k, const void* v, void* o
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.lse = nullptr;
   a.plan = nullptr;
+  a.du = nullptr;
+  a.nblk = nullptr;
+  a.starts = nullptr;
+  a.plan_out = nullptr;
   a.B = batch; a.Hq = hq; a.Hkv = hkv; a.n = n; a.s = 1;
   a.ntile = (n + BM - 1) / BM;
   const int grid = grid_size(a.ntile, batch * hq, &a.cs);

@@ -1,4 +1,4 @@
-// Device code shared by the attention kernels (attn.hip, stream.hip): tile
+// Device code of the attention kernels (attn.hip): tile
 // geometry, LDS helpers, the K/V tile loader and the per-chunk computation of
 // the count-weighted attention (logits, counts, softmax, value product).
 //
@@ -53,6 +53,15 @@ struct FwdArgs {
   const void* q; const void* k; const void* v; void* o;
   const PlanRec* plan;
   float* lse;  // optional: log of each row's normaliser, [B, Hq, n]
+  // Plan in the kernel (count-weighted mode, when du is not null): each
+  // workgroup evaluates the bins of its query tile from the (delta, u)
+  // pairs du[2 (h s + i)], du[2 (h s + i) + 1] instead of reading `plan`,
+  // and the workgroups of batch row 0 write the bin buffer's block counts,
+  // block starts and plan records (the bin kernel's output, bit for bit).
+  const double* du;
+  int32_t* nblk;
+  int32_t* starts;
+  PlanRec* plan_out;
   int B, Hq, Hkv, n, s, ntile, cs;
 };
 
@@ -82,7 +91,9 @@ constexpr int SM_LO = 256;
 constexpr int SM_HI = SM_LO + 4 * BM;
 constexpr int SM_SORT = SM_HI + 4 * BM;      // 4 x 128 ints: a, e in a order; e2, a2 in e2 order
 constexpr int SM_KEYS = SM_SORT + 4 * 4 * 128;  // 2 x 128 ints: the sort keys (a; -e2)
-constexpr int SMALL = SM_KEYS + 2 * 4 * 128;
+constexpr int SM_REC = SM_KEYS + 2 * 4 * 128;  // 128 x 32 bytes: plan records evaluated in the kernel
+constexpr int SM_BASE = SM_REC + 32 * 128;  // 128 ints: block index of row r0's block, per hash
+constexpr int SMALL = SM_BASE + 4 * 128;
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,

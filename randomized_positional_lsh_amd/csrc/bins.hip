@@ -23,6 +23,7 @@
 // its predecessor; position 0 always starts a block.
 #include <climits>
 
+#include "bins_device.h"
 #include "internal.h"
 
 namespace plpsh {
@@ -30,82 +31,6 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-
-// Bin of position x from the product with a rounded reciprocal, which is
-// within 2.2 ulp of the quotient: where no integer lies within 2^-50 |q| of
-// it the floor equals that of the correctly rounded quotient, and the
-// function returns true (certified).
-__device__ __forceinline__ bool certified_bin(int x, double u, double rinv, double* f) {
-  const double q = (static_cast<double>(x) - u) * rinv;
-  const double fl = floor(q);
-  const double fr = q - fl;  // exact for |q| < 2^52
-  const double margin = fabs(q) * 0x1p-50;
-  *f = fl;
-  return fr > margin && fr < 1.0 - margin;
-}
-
-// Start flags of the 32 positions x0 .. x0 + 31 (bit b: bin(x0 + b) differs
-// from bin(x0 + b - 1)), bins evaluated in binary64 as floor((x - u) / delta).
-//
-// Wide hashes (delta >= 32, the same for the whole workgroup, so the branch
-// does not diverge): computed bins never decrease with x (the rounded
-// subtraction and division are monotone), and the bins of x0 - 1 and
-// x0 + 31 differ by at most one.  Equal bins mean no start in the word;
-// bins one apart mean exactly one start, found by bisection (5 more
-// evaluations).  Everything else, and any evaluation that is not
-// certified, takes the general pass: all 33 bins by certified products,
-// and if one of them misses the margin (rare), the division itself.
-// The general pass is fully unrolled so that the evaluations overlap.
-__device__ __forceinline__ uint32_t start_flags(int x0, double u, double delta, double rinv, bool wide) {
-  if (wide) {
-    double fa, fb;
-    bool ok = certified_bin(x0 - 1, u, rinv, &fa);
-    ok = certified_bin(x0 + 31, u, rinv, &fb) && ok;
-    if (ok && fa == fb) return 0u;
-    if (ok && fb == fa + 1.0) {
-      int lo = -1, hi = 31;  // bin(x0 + lo) = fa, bin(x0 + hi) = fb
-#pragma unroll
-      for (int it = 0; it < 5; ++it) {
-        const int mid = (lo + hi) >> 1;
-        double fm;
-        ok = certified_bin(x0 + mid, u, rinv, &fm) && ok;
-        if (fm == fb) hi = mid; else lo = mid;
-      }
-      if (ok) return 1u << hi;
-    }
-  }
-  // The 33 bins from one product and then one fused multiply-add each:
-  // q_k = k rinv + q_0 lies within 36 2^-53 max(|q_0|, |q_k|, 32 / delta) of
-  // the exact quotient (q_0's three roundings, k times the reciprocal's, the
-  // fma's own), and the binary64 quotient of the definition within 2^-52 |q|
-  // of it, so a fractional part farther than 2^-47 max(|q_0|, |q_32|,
-  // 32 rinv) from an integer settles the floor.
-  const double q0 = (static_cast<double>(x0 - 1) - u) * rinv;
-  const double margin = 0x1p-47 * fmax(fmax(fabs(q0), fabs(fma(32.0, rinv, q0))), 32.0 * rinv);
-  double f[33];
-  bool exact = false;
-#pragma unroll
-  for (int k = 0; k < 33; ++k) {
-    const double q = fma(static_cast<double>(k), rinv, q0);
-    const double fl = floor(q);
-    const double fr = q - fl;  // exact for |q| < 2^52
-    f[k] = fl;
-    exact = exact || !(fr > margin && fr < 1.0 - margin);
-  }
-  uint32_t m = 0u;
-  if (!exact) {
-#pragma unroll
-    for (int b = 0; b < 32; ++b) m |= static_cast<uint32_t>(f[b + 1] != f[b]) << b;
-  } else {
-    double prev = floor((static_cast<double>(x0 - 1) - u) / delta);
-    for (int b = 0; b < 32; ++b) {
-      const double bb = floor((static_cast<double>(x0 + b) - u) / delta);
-      m |= static_cast<uint32_t>(bb != prev) << b;
-      prev = bb;
-    }
-  }
-  return m;
-}
 
 // Exclusive scan of one int per thread over the workgroup.
 __device__ int wg_exclusive_scan(int v, int* wsum, int* total) {
@@ -152,7 +77,8 @@ __global__ __launch_bounds__(kThreads) void bins_kernel(const double* __restrict
     uint32_t m = 0u;
     if (w < nused) {
       const int x0 = 32 * w;
-      m = start_flags(x0, u, delta, rinv, wide);
+      double prev;
+      m = start_flags(x0, u, delta, rinv, wide, &prev);
       if (x0 == 0) m |= 1u;
       if (n - x0 < 32) m &= (1u << (n - x0)) - 1u;
     }
@@ -250,35 +176,6 @@ constexpr int kPartThreads = 256;
 constexpr int kPartWords = 256;  // 32-position words per part, one per thread; a multiple of 4, so
                                  // that the four words of a 128-row tile lie in one part
 
-// The bin of x by its definition (binary64 difference, quotient, floor).
-__device__ __forceinline__ double exact_bin(int x, double u, double delta) {
-  return floor((static_cast<double>(x) - u) / delta);
-}
-
-// Smallest x in [0, n] with bin(x) >= k (n if there is none).  Bins never
-// decrease with x; the real-number answer ceil(k delta + u) is taken as the
-// first guess, rounding moves the answer by at most a position or two, and a
-// bisection settles anything further.
-__device__ int first_at_least(double k, double u, double delta, int n) {
-  const double gd = ceil(fma(k, delta, u));
-  int g = gd <= 0.0 ? 0 : (gd >= static_cast<double>(n) ? n : static_cast<int>(gd));
-  for (int it = 0; it < 4; ++it) {
-    if (g > 0 && exact_bin(g - 1, u, delta) >= k) {
-      --g;
-    } else if (g < n && exact_bin(g, u, delta) < k) {
-      ++g;
-    } else {
-      return g;
-    }
-  }
-  int lo = 0, hi = n;  // the answer lies in [lo, hi]
-  while (lo < hi) {
-    const int mid = lo + (hi - lo) / 2;
-    if (exact_bin(mid, u, delta) >= k) hi = mid; else lo = mid + 1;
-  }
-  return lo;
-}
-
 // Exclusive scan of one int per thread over a kPartThreads workgroup.
 __device__ int part_exclusive_scan(int v, int* wsum, int* total) {
   constexpr int kW = kPartThreads / 64;
@@ -331,7 +228,8 @@ __global__ __launch_bounds__(kPartThreads) void bins_part_kernel(const double* _
   uint32_t m = 0u;
   if (w < nused) {
     const int x0 = 32 * w;
-    m = every ? ~0u : start_flags(x0, u, delta, rinv, wide);
+    double prev;
+    m = every ? ~0u : start_flags(x0, u, delta, rinv, wide, &prev);
     if (x0 == 0) m |= 1u;
     if (n - x0 < 32) m &= (1u << (n - x0)) - 1u;
   }
@@ -373,10 +271,10 @@ __global__ __launch_bounds__(kPartThreads) void bins_part_kernel(const double* _
       rec.e2 = rl + 1;
     } else {
       const double k0 = exact_bin(r0, u, delta), k1 = exact_bin(rl, u, delta);
-      rec.a = first_at_least(k0, u, delta, n);
-      rec.e = first_at_least(k0 + 1.0, u, delta, n);
-      rec.a2 = first_at_least(k1, u, delta, n);
-      rec.e2 = first_at_least(k1 + 1.0, u, delta, n);
+      rec.a = first_at_least(k0, u, delta, rinv, n);
+      rec.e = first_at_least(k0 + 1.0, u, delta, rinv, n);
+      rec.a2 = first_at_least(k1, u, delta, rinv, n);
+      rec.e2 = first_at_least(k1 + 1.0, u, delta, rinv, n);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) rec.bits[j] = wd[4 * tid + j].x;

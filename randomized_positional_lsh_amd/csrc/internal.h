@@ -61,10 +61,14 @@ void draw_hash(uint64_t seed, int h, int i, double sigma, double* delta, double*
 bool bins_near_one(const double* delta, long long count);
 hipError_t launch_bins(const double* du, int heads, int s, int n, void* bins, bool near_one, hipStream_t st);
 
+// du (device-readable interleaved (delta, u) pairs, count-weighted mode
+// only): the kernel evaluates its own plan records and writes the whole bin
+// buffer `bins` (no delta may lie within 2^-30 of 1); null: it reads the
+// records of a bin buffer that the bin kernel wrote.
 hipError_t launch_plsh_fwd(const void* q, const void* k, const void* v, void* o,
                            int batch, int hq, int hkv, int n, int d, int dtype,
                            int s, int causal, const void* bins, const uint16_t* head_order,
-                           bool literal, float* lse, hipStream_t st);
+                           bool literal, float* lse, hipStream_t st, const double* du = nullptr);
 
 hipError_t launch_alibi_fwd(const void* q, const void* k, const void* v, void* o,
                             int batch, int hq, int hkv, int n, int d, int dtype,

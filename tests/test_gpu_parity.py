@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 import synth
+from tests._parity import check_bins as _check_bins
 from tests._parity import check_slices, oracle_full, oracle_hashes, sample_rows, say, to64
 
 pytestmark = pytest.mark.gpu
@@ -33,45 +34,6 @@ def _qkv_dev(B, Hq, Hkv, n, d, dtype, seed, gpu, scale_q=1.0):
 
 
 # ------------------------------------------------------------------ bins --
-
-def _expected_plan(delta, u, n, tiles=None):
-    """Block starts and the plan records of `tiles` (all tiles if None; the
-    other rows of the returned array are left zero)."""
-    st = oracle.block_starts(delta, u, n)
-    ntile = (n + 127) // 128
-    rec = np.zeros((ntile, 8), dtype=np.int64)
-    starts_set = set(st.tolist()) | {n}
-    for q in (range(ntile) if tiles is None else tiles):
-        r0 = 128 * q
-        rl = min(r0 + 127, n - 1)
-        a, e = oracle.block_of(delta, u, n, [r0, rl])
-        rec[q, 0], rec[q, 1], rec[q, 2], rec[q, 3] = a[0], e[0], a[1], e[1]
-        bits = [0, 0, 0, 0]
-        for p in range(1, 128):
-            if r0 + p in starts_set:
-                bits[p >> 5] |= 1 << (p & 31)
-        rec[q, 4:] = bits
-    return st, rec
-
-
-def _check_bins(bins, delta, u, n, tiles=None):
-    """Block counts and starts of every hash, and the plan records of `tiles`
-    (every tile if None), bit-exact against the oracle."""
-    nblk = bins.nblk.cpu().numpy()
-    starts = bins.starts.cpu().numpy()
-    plan = bins.plan.cpu().numpy().view(np.uint32).astype(np.int64)
-    H, s = delta.shape
-    sel = slice(None) if tiles is None else np.asarray(tiles)
-    for h in range(H):
-        for i in range(s):
-            t = h * s + i
-            st, rec = _expected_plan(delta[h, i], u[h, i], n, tiles)
-            assert nblk[t] == st.size, (h, i, delta[h, i], u[h, i], n)
-            assert np.array_equal(starts[t, :st.size + 1], np.append(st, n)), (h, i, delta[h, i], u[h, i], n)
-            got = plan[h, :, i, :].copy()
-            got[:, :4] = plan[h, :, i, :4].astype(np.uint32).view(np.int32)
-            assert np.array_equal(got[sel], rec[sel]), (h, i, delta[h, i], u[h, i], n)
-
 
 # Widths within 2^-30 of 1 send the whole launch to the per-hash bin kernel;
 # all others take the part kernel, whose start counts have a closed form
