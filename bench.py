@@ -20,8 +20,9 @@ Prints ONE JSON line.  Besides the contract fields it carries:
                  groups of 5 steps, an event at each group boundary)
   two_launch   : the same step as two launches (plpsh_sample_bins, whose
                  bin kernel writes the buffer, then plpsh_attention_fwd_bins)
-  roofline     : the attention kernel against the HBM roofline: algorithmic
-                 bytes (Q, K, V read once + O written once, per launch)
+  roofline     : the step's kernel against the HBM roofline: algorithmic
+                 bytes (Q, K, V read once + O and the bin buffer written
+                 once, per launch)
                  divided by the kernel's median duration with the L2 and the
                  last-level cache evicted (by a read-only pass over 512 MiB)
                  before each launch (the roofline
@@ -86,6 +87,15 @@ def algorithmic_bytes(W) -> int:
     """Q, K, V read once and O written once (bytes per launch)."""
     eb = 2 if W.dtype == "bf16" else 4
     return eb * W.batch * W.n * W.head_dim * (2 * W.heads_q + 2 * W.heads_kv)
+
+
+def bin_buffer_bytes(W, P, ws) -> int:
+    """Bytes of the bin buffer that the one-launch kernel writes besides O:
+    the block counts, every block start with its closing entry n (counted
+    from the counts of this draw), and the plan records."""
+    nblk = P.Bins(ws, W.heads_q, W.s, W.n).nblk.cpu().numpy().astype(int)
+    ntile = (W.n + 127) // 128
+    return 4 * nblk.size + 4 * int((nblk + 1).sum()) + 32 * W.heads_q * ntile * W.s
 
 
 def useful_flops(W, P, ws) -> float:
@@ -443,11 +453,12 @@ def long_point(P, synth, dev, dense_ms, steps=5):
     wall = time_steps(run, steps, 2)
     ms = 1e3 * wall / steps
     kms = float(np.median(kernel_times(run, 5, cold=True)))
+    abytes = algorithmic_bytes(W) + bin_buffer_bytes(W, P, run.ws)
     del q, k, v, run
     torch.cuda.empty_cache()
     out = {"workload": "long-context", "n": W.n, "s": W.s, "plsh_ms": round(ms, 4),
            "kernel_ms_cold_cache": round(kms, 4), "tokens_per_s": round(W.batch * W.n / (ms * 1e-3), 1),
-           "hbm_frac_cold_cache": round(algorithmic_bytes(W) / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+           "hbm_frac_cold_cache": round(abytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     if dense_ms is not None:
         out["dense_ms"] = round(dense_ms, 4)
         out["speedup_plsh_vs_dense"] = round(dense_ms / ms, 2)
@@ -467,13 +478,14 @@ def workload_point(P, synth, dev, name, steps=20):
     ms = 1e3 * wall / steps
     cold = float(np.median(kernel_times(run, 10, cold=True)))
     warm = float(np.median(kernel_times(run, 10, cold=False)))
+    abytes = algorithmic_bytes(W) + bin_buffer_bytes(W, P, run.ws)
     del q, k, v, run
     torch.cuda.empty_cache()
     return {"batch": W.batch, "heads_q": W.heads_q, "heads_kv": W.heads_kv, "n": W.n, "head_dim": W.head_dim,
             "dtype": W.dtype, "s": W.s, "causal": W.causal, "step_ms": round(ms, 5),
             "tokens_per_s": round(W.batch * W.n / (ms * 1e-3), 1), "kernel_ms_cold_cache": round(cold, 5),
             "kernel_ms_warm": round(warm, 5),
-            "hbm_frac_cold_cache": round(algorithmic_bytes(W) / (cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            "hbm_frac_cold_cache": round(abytes / (cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def convergence(P, dev, n=131072, sigma=256.0, ss=(2, 4, 8, 16, 32, 64, 128), seeds=3, max_steps=400):
@@ -592,7 +604,8 @@ def main():
 
     delta = run.delta.reshape(W.heads_q, W.s).copy()
     u = run.u.reshape(W.heads_q, W.s).copy()
-    abytes = algorithmic_bytes(W)
+    bbytes = bin_buffer_bytes(W, P, run.ws)
+    abytes = algorithmic_bytes(W) + bbytes
     achieved = abytes / (kern_ms * 1e-3) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -607,6 +620,7 @@ def main():
                 "kernel": "plpsh fwd_kernel (bins of each query tile + attention)",
                 "cache": "L2 and last-level cache evicted before each launch",
                 "kernel_ms": round(kern_ms, 5), "kernel_ms_pct": pct(cold), "algorithmic_bytes": abytes,
+                "bin_buffer_bytes": bbytes,
                 "useful_tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                 "kernel_ms_warm": round(warm_ms, 5), "kernel_ms_warm_pct": pct(warm),
                 "frac_warm": round(abytes / (warm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
