@@ -175,7 +175,11 @@ size_t plpsh_workspace_bytes(int32_t heads_q, int32_t s, int32_t n);
  * plpsh_attention_fwd -- Positional-LSH ALiBi attention, forward pass
  * (Theorem 2.2 with M~ of Theorem 2.1).  Draws s hashes per query head from
  * `seed` on the host, computes their blocks on the device, then
- * O = count-weighted attention (formula at the top of this file).
+ * O = count-weighted attention (formula at the top of this file).  One
+ * kernel launch does both (each workgroup evaluates the bins of its own
+ * query tile) unless some width lies within 2^-30 of 1, when the bin kernel
+ * runs first; either way the workspace receives the bin buffer exactly as
+ * plpsh_sample_bins writes it (block counts, block starts, plan records).
  *
  *   q, o     : device [batch, heads_q,  n, head_dim], contiguous, d innermost
  *   k, v     : device [batch, heads_kv, n, head_dim], contiguous
@@ -263,8 +267,9 @@ plpsh_status plpsh_fixed_blocks_fwd(const void* q, const void* k, const void* v,
 /*
  * plpsh_attention_fwd_bins -- the attention step alone, on a bin buffer
  * already computed by plpsh_sample_bins / plpsh_bins_from_hashes for the
- * same (heads_q, s, n).  plpsh_attention_fwd is exactly plpsh_sample_bins
- * followed by this call; splitting them lets one draw serve several calls.
+ * same (heads_q, s, n).  plpsh_attention_fwd gives exactly the results of
+ * plpsh_sample_bins followed by this call (bit for bit: output and bin
+ * buffer); splitting them lets one draw serve several calls.
  *
  *   bins   : device, >= plpsh_bins_bytes(heads_q, s, n) bytes, 256-byte
  *            aligned, written by the bin kernel for these sizes (the
