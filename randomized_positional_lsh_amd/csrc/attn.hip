@@ -56,33 +56,50 @@
 namespace plpsh {
 namespace {
 
+// Tasks of the in-kernel plan: 4 s start-flag tasks (word q = 0..3 of the
+// tile, hash i) on waves 0-3 and 4 s bound tasks (a, e, a2, e2 of hash i) on
+// waves 4-7, task t = q s + i, lane l of wave w taking t = 64 (w mod 4) + l
+// (pass 0) and t + 256 (pass 1, more than 64 hashes).  Packing the tasks into
+// whole waves leaves the waves with no task free of the plan's arithmetic
+// (at s = 20: two waves of each kind work, not eight).  Returns whether the
+// lane has a task in the pass; q and i are then its part and hash.
+__device__ __forceinline__ bool plan_task(int w, int lane, int pass, int s, int& q, int& i) {
+  const int t = 64 * (w & 3) + lane + 256 * pass;
+  q = (t >= s) + (t >= 2 * s) + (t >= 3 * s);
+  i = t - q * s;
+  return t < 4 * s;
+}
+// whether wave w has any task in the pass (wave-uniform)
+__device__ __forceinline__ bool plan_wave_busy(int w, int pass, int s) { return 64 * (w & 3) + 256 * pass < 4 * s; }
+
 // Plan records of query tile r0 .. r0 + 127 for the hashes of head h,
-// evaluated from (delta, u) (bins_device.h): the record of hash i goes to
+// evaluated from (delta, u) (bins_device.h), hd/hu holding the pair of the
+// lane's task in each pass (plan_task): the record of hash i goes to
 // srec + 32 i, in the layout of PlanRec, and the block index of row r0's
 // block, bin(r0) - bin(0) (r0 when every position starts a block), to
-// sbase[i].  Waves 0-3 take the start flags of the tile's 32-position words
-// 0-3, waves 4-7 the block bounds a, e (block of row r0) and a2, e2 (block
-// of the last row); lane l takes hashes l and l + 64.  In the last tile the
-// workgroup of batch row 0 writes the block count and the closing entry n
-// of the bin buffer (scatter_starts below writes the starts).  The launcher
-// sends no delta within 2^-30 of 1 here (there the start count has no
-// closed form).
+// sbase[i].  Flag tasks take the start flags of the tile's 32-position word
+// q, bound tasks the block bounds a, e (block of row r0; q = 0, 1) or a2, e2
+// (block of the last row; q = 2, 3).  In the last tile the workgroup of
+// batch row 0 writes the block count and the closing entry n of the bin
+// buffer (scatter_starts below writes the starts).  The launcher sends no
+// delta within 2^-30 of 1 here (there the start count has no closed form).
 template <bool CAUSAL, int NCH>
 __device__ __forceinline__ void plan_tile(const FwdArgs& A, const double (&hd)[2], const double (&hu)[2], int h,
                                           int b, int qt, int r0, int n, int s, int w, int lane,
                                           unsigned char* srec, int* sbase) {
   const int rl = min(r0 + BM - 1, n - 1);
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    if (x == 1 && NCH != 4) break;
-    const int i = lane + 64 * x;
-    if (i >= s) continue;
-    const double delta = hd[x], u = hu[x];
+  for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 1 && NCH != 4) break;
+    if (!plan_wave_busy(w, pass, s)) break;
+    int q, i;
+    if (!plan_task(w, lane, pass, s, q, i)) continue;
+    const double delta = hd[pass], u = hu[pass];
     const bool every = delta <= 1.0 - 0x1p-30;
     const double rinv = 1.0 / delta;
     uint32_t* rec = reinterpret_cast<uint32_t*>(srec + 32 * i);
     if (w < 4) {
-      const int x0 = r0 + 32 * w;
+      const int x0 = r0 + 32 * q;
       uint32_t m = 0u;
       if (x0 < n) {
         double prev;
@@ -90,18 +107,17 @@ __device__ __forceinline__ void plan_tile(const FwdArgs& A, const double (&hd)[2
         if (n - x0 < 32) m &= (1u << (n - x0)) - 1u;
       }
       // bit p: position r0 + p (1 <= p < 128) starts a block, or equals n
-      if (w == 0) m &= ~1u;
+      if (q == 0) m &= ~1u;
       const int p = n - r0;
-      if (p < BM && (p >> 5) == w) m |= 1u << (p & 31);
-      rec[4 + w] = m;
+      if (p < BM && (p >> 5) == q) m |= 1u << (p & 31);
+      rec[4 + q] = m;
     } else {
-      const int j = w - 4;
-      const int r = j < 2 ? r0 : rl;
+      const int r = q < 2 ? r0 : rl;
       const double kr = every ? 0.0 : bin_at(r, u, delta, rinv);
-      const int val = every ? r + (j & 1) : first_at_least(kr + static_cast<double>(j & 1), u, delta, rinv, n);
-      rec[j] = static_cast<uint32_t>(val);
-      if (j == 1) sbase[i] = every ? r0 : static_cast<int>(kr - exact_bin(0, u, delta));
-      if (j == 3 && b == 0 && A.starts != nullptr && qt == A.ntile - 1) {
+      const int val = every ? r + (q & 1) : first_at_least(kr + static_cast<double>(q & 1), u, delta, rinv, n);
+      rec[q] = static_cast<uint32_t>(val);
+      if (q == 1) sbase[i] = every ? r0 : static_cast<int>(kr - exact_bin(0, u, delta));
+      if (q == 3 && b == 0 && A.starts != nullptr && qt == A.ntile - 1) {
         const int nb = every ? n : static_cast<int>(exact_bin(n - 1, u, delta) - exact_bin(0, u, delta)) + 1;
         A.nblk[h * s + i] = nb;
         A.starts[static_cast<size_t>(h * s + i) * (n + 1) + nb] = n;
@@ -114,31 +130,32 @@ __device__ __forceinline__ void plan_tile(const FwdArgs& A, const double (&hd)[2
 // indices in the bin buffer, from the records plan_tile left in LDS: bins
 // rise by one at each start, so the tile's starts take consecutive indices,
 // the first one that of row r0's block if it starts at r0, else the next.
-// Waves 0-3 take words 0-3 of the tile, lane l hashes l and l + 64.
-template <int NCH>
-__device__ __forceinline__ void scatter_starts(const FwdArgs& A, int h, int r0, int n, int s, int w, int lane,
-                                               const unsigned char* srec, const int* sbase) {
-  if (w >= 4) return;
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    if (x == 1 && NCH != 4) break;
-    const int i = lane + 64 * x;
-    if (i >= s) continue;
+// The wave takes hashes i0, i0 + di, ...; lane l writes the starts at
+// positions r0 + l and r0 + 64 + l, each at the first index plus the number
+// of starts before it in the tile (a masked bit count), so that every store
+// instruction writes consecutive entries of one hash.
+__device__ __forceinline__ void scatter_starts(const FwdArgs& A, int h, int r0, int n, int s, int i0, int di,
+                                               int lane, const unsigned char* srec, const int* sbase) {
+  const int p = n - r0;  // the closing bit (position n), not a start
+  for (int i = i0; i < s; i += di) {
     const uint32_t* rec = reinterpret_cast<const uint32_t*>(srec + 32 * i);
-    const int p = n - r0;  // the closing bit (position n), not a start
-    const bool r0s = static_cast<int>(rec[0]) == r0;  // row r0's block starts at r0
-    int o = sbase[i] + (r0s ? 0 : 1);
-    uint32_t m = 0u;
+    const bool r0s = __builtin_amdgcn_readfirstlane(static_cast<int>(rec[0])) == r0;  // row r0's block starts at r0
+    uint32_t bv[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      uint32_t bv = rec[4 + v];
-      if (p < BM && (p >> 5) == v) bv &= ~(1u << (p & 31));
-      if (v == 0 && r0s) bv |= 1u;
-      if (v < w) o += __builtin_popcount(bv);
-      if (v == w) m = bv;
+      bv[v] = __builtin_amdgcn_readfirstlane(rec[4 + v]);
+      if (p < BM && (p >> 5) == v) bv[v] &= ~(1u << (p & 31));
     }
-    int32_t* st = A.starts + static_cast<size_t>(h * s + i) * (n + 1);
-    for (; m != 0u; m &= m - 1u) st[o++] = r0 + 32 * w + __builtin_ctz(m);
+    if (r0s) bv[0] |= 1u;
+    const int o = __builtin_amdgcn_readfirstlane(sbase[i]) + (r0s ? 0 : 1);
+    int32_t* st = A.starts + static_cast<size_t>(h * s + i) * (n + 1) + o;
+    const int k0 = static_cast<int>(__builtin_amdgcn_mbcnt_hi(bv[1], __builtin_amdgcn_mbcnt_lo(bv[0], 0u)));
+    const int k1 = __builtin_popcount(bv[0]) + __builtin_popcount(bv[1]) +
+                   static_cast<int>(__builtin_amdgcn_mbcnt_hi(bv[3], __builtin_amdgcn_mbcnt_lo(bv[2], 0u)));
+    const uint32_t b0 = lane < 32 ? bv[0] >> lane : bv[1] >> (lane - 32);
+    const uint32_t b1 = lane < 32 ? bv[2] >> lane : bv[3] >> (lane - 32);
+    if (b0 & 1u) st[k0] = r0 + lane;
+    if (b1 & 1u) st[k1] = r0 + 64 + lane;
   }
 }
 
@@ -195,17 +212,19 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
   u32x4 pb[2];                                 // boundary bits
   u32x4 pr[2];                                 // a, e, a2, e2
   int lo = 0, hi = n, cntA = 0;
-  // in-kernel plan: (delta, u) of hashes lane and lane + 64, else plan records
+  // in-kernel plan: (delta, u) of the lane's plan tasks (plan_task), else plan records
   const bool inplan = PL && A.du != nullptr;
   double hd[2] = {1.0, 1.0}, hu[2] = {0.0, 0.0};
   if (inplan) {
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int i = lane + 64 * x;
-      const bool ok = (x == 0 || NCH == 4) && i < s;
-      const double* p = A.du + 2 * (static_cast<size_t>(h) * s + (i < s ? i : 0));
-      hd[x] = ok ? p[0] : 1.0;
-      hu[x] = ok ? p[1] : 0.0;
+    for (int pass = 0; pass < 2; ++pass) {
+      if (pass == 1 && NCH != 4) break;
+      if (!plan_wave_busy(w, pass, s)) break;
+      int q, i;
+      const bool ok = plan_task(w, lane, pass, s, q, i);
+      const double* p = A.du + 2 * (static_cast<size_t>(h) * s + (ok ? i : 0));
+      hd[pass] = ok ? p[0] : 1.0;
+      hu[pass] = ok ? p[1] : 0.0;
     }
   } else if constexpr (PL || LIT) {
     const size_t tix = static_cast<size_t>(h) * A.ntile + qt;
@@ -426,6 +445,12 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
           sv[i] = by_a ? INT_MIN : INT_MAX;
         }
       }
+    } else if (inplan && b == 0 && A.starts != nullptr) {
+      // the tile's block starts in the bin buffer (in-kernel plan, batch row
+      // 0), by the waves that do not sort, while the sort runs
+      const int nsort = CAUSAL ? 1 : 2;  // waves NW - 4 (and NW - 3) sort
+      scatter_starts(A, h, r0, n, s, w < NW - 4 ? w : w - nsort, NW - nsort, lane, sm + SM_REC,
+                     reinterpret_cast<const int*>(sm + SM_BASE));
     }
     lds_barrier();
     // H operand through transposing reads of the [position][row] matrix:
@@ -743,12 +768,6 @@ __global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) *
         *reinterpret_cast<f32x4*>(orow + 16 * db + 4 * g) = o;
       }
     }
-  }
-  // the tile's block starts in the bin buffer (in-kernel plan, batch row 0),
-  // off the set-up's path
-  if constexpr (PL) {
-    if (inplan && b == 0 && A.starts != nullptr)
-      scatter_starts<NCH>(A, h, r0, n, s, w, lane, sm + SM_REC, reinterpret_cast<const int*>(sm + SM_BASE));
   }
 }
 
