@@ -389,22 +389,26 @@ __global__ __launch_bounds__(NT, 2) void bwd_kernel(BwdArgs A, BwdOrder ord) {
     const int loF = __builtin_amdgcn_readlane(lo_own, 0);
     const int hiL = __builtin_amdgcn_readlane(hi_own, 15);
 
-    // own-side count factors over hash slots 32 ch + 8 g .. + 7:
-    // left of the own tile [own < e], right of it [own >= a2]
+    // own-side count factors over hash slots 32 ch + 8 g .. + 7: left of
+    // the own tile [own < e], right of it [own >= a2].  Each is built right
+    // before its phase, so that it does not sit beside the near-count
+    // operand (or the other factor) in registers.
     u32x4 fl[NCH], fr[NCH];
+    auto own_factors = [&](bool right, u32x4 (&f)[NCH]) {
 #pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-      const unsigned char* hp = sm + SM_HASH + 16 * (32 * ch + 8 * g);
+      for (int ch = 0; ch < NCH; ++ch) {
+        const unsigned char* hp = sm + SM_HASH + 16 * (32 * ch + 8 * g);
 #pragma unroll
-      for (int u2 = 0; u2 < 4; ++u2) {
-        const u32x4 r0v = *reinterpret_cast<const u32x4*>(hp + 16 * (2 * u2));
-        const u32x4 r1v = *reinterpret_cast<const u32x4*>(hp + 16 * (2 * u2 + 1));
-        fl[ch][u2] = (own < static_cast<int>(r0v[1]) ? 0x3F80u : 0u) |
-                     (own < static_cast<int>(r1v[1]) ? 0x3F800000u : 0u);
-        fr[ch][u2] = (own >= static_cast<int>(r0v[2]) ? 0x3F80u : 0u) |
-                     (own >= static_cast<int>(r1v[2]) ? 0x3F800000u : 0u);
+        for (int u2 = 0; u2 < 4; ++u2) {
+          const u32x4 r0v = *reinterpret_cast<const u32x4*>(hp + 16 * (2 * u2));
+          const u32x4 r1v = *reinterpret_cast<const u32x4*>(hp + 16 * (2 * u2 + 1));
+          f[ch][u2] = right ? ((own >= static_cast<int>(r0v[2]) ? 0x3F80u : 0u) |
+                               (own >= static_cast<int>(r1v[2]) ? 0x3F800000u : 0u))
+                            : ((own < static_cast<int>(r0v[1]) ? 0x3F80u : 0u) |
+                               (own < static_cast<int>(r1v[1]) ? 0x3F800000u : 0u));
+        }
       }
-    }
+    };
     // dQ: the own row's LSE (log2 units) and D
     float lse2_own = 0.f, dd_own = 0.f;
     if constexpr (!KEYSIDE) {
@@ -590,10 +594,14 @@ __global__ __launch_bounds__(NT, 2) void bwd_kernel(BwdArgs A, BwdOrder ord) {
     };
     int t = 0;
     for (; t < nnear; ++t) tile(std::integral_constant<int, 0>{}, t);
-    if constexpr (!CAUSAL || !KEYSIDE)  // other before own: dQ, or no causal cut
+    if constexpr (!CAUSAL || !KEYSIDE) {  // other before own: dQ, or no causal cut
+      if (nleft > 0) own_factors(false, fl);
       for (; t < nnear + nleft; ++t) tile(std::integral_constant<int, 1>{}, t);
-    if constexpr (!CAUSAL || KEYSIDE)   // other after own: dK/dV, or no causal cut
+    }
+    if constexpr (!CAUSAL || KEYSIDE) {  // other after own: dK/dV, or no causal cut
+      if (nright > 0) own_factors(true, fr);
       for (; t < ntl; ++t) tile(std::integral_constant<int, 2>{}, t);
+    }
   }
 
   // ---- epilogue: Acc1 is dQ^T or dK^T (times sqrt(d) too much), Acc2 dV^T
