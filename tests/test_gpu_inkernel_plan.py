@@ -144,3 +144,29 @@ def test_near_one_widths_take_the_bin_kernel(gpu, n, causal):
     if n <= 1000:
         err = check_slices(to64(o1), oracle_full(q64, k64, v64, delta, u, causal), "bf16", where=f"n={n}")
         say(f"  max err {err:.3e}")
+
+
+@pytest.mark.parametrize("s", [1, 15, 16, 17, 31, 32, 33, 48, 63, 64, 65, 96, 127, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["nc", "c"])
+def test_plan_task_wave_boundaries(gpu, s, causal):
+    """The plan's 4 s flag tasks and 4 s bound tasks fill whole waves (64
+    tasks each, a second pass past 256): hash counts on both sides of every
+    wave boundary (4 s = 64, 128, 192, 256) and of the second pass give the
+    bin buffer bit for bit and the two-launch output."""
+    n = 700
+    rng = np.random.default_rng(1000 + s)
+    H = 2
+    sig = np.array([3.0, 90.0])
+    delta = rng.gamma(2.0, 1.0, size=(H, s)) * sig[:, None]
+    delta = np.where(np.abs(delta - 1.0) < 2 ** -29, 1.5, delta)
+    u = delta * rng.uniform(size=(H, s))
+    say(f"plan task boundaries s={s} causal={causal}")
+    (q, k, v), (q64, k64, v64) = _qkv(1, H, 1, n, 64, "bf16", 31 + s, gpu)
+    o1, bins = _one_launch(q, k, v, delta, u, causal)
+    o2 = _two_launch(q, k, v, delta, u, causal)
+    torch.cuda.synchronize()
+    check_bins(bins, delta, u, n)
+    assert torch.equal(o1, o2), "one-launch output differs from the two-launch path"
+    if s in (17, 65):
+        err = check_slices(to64(o1), oracle_full(q64, k64, v64, delta, u, causal), "bf16", where=f"s={s}")
+        say(f"  max err {err:.3e}")
