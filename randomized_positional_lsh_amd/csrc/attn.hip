@@ -45,8 +45,11 @@
 //
 // Softmax: one running row maximum shared by all hashes.  It is raised only
 // when a tile exceeds it by more than 2^8 in the exponential, so rescaling
-// is rare; masked entries (c = 0, or j > r when causal) enter as -inf; the
-// first tile holds the diagonal, where c = s > 0.
+// is rare.  In the near tiles masked entries (c = 0, or j > r when causal)
+// enter as -inf; they hold the diagonal, where c = s > 0, so every row's
+// maximum is finite before the far tiles, where the mask is applied only in
+// the (rare) chunks that trigger a raise: otherwise every exponent is at
+// most 8 and an uncounted entry weighs 2^t * 0 = 0.
 //
 // MODE_ALIBI computes exact dense ALiBi attention, weight e^{S - |r-j|/sigma},
 // over every key with the same pipeline.

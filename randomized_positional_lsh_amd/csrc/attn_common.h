@@ -340,8 +340,6 @@ struct Fwd {
     // weights in log2 units (ALiBi) or logits (PLSH); masking; local maxima
     float lmx[NRB];
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) lmx[rb] = -INFINITY;
-#pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
@@ -352,7 +350,7 @@ struct Fwd {
           if constexpr (MODE == MODE_ALIBI) x = fmaf(x, sc, -beta * fabsf(static_cast<float>(R[rb] - J)));
           sacc[kb2][rb][e] = x;
         }
-    if (!inside) {
+    auto mask = [&]() {
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
@@ -370,18 +368,37 @@ struct Fwd {
             }
             sacc[kb2][rb][e] = ok ? sacc[kb2][rb][e] : -INFINITY;
           }
-    }
+    };
+    auto row_max = [&]() {
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
+      for (int rb = 0; rb < NRB; ++rb) {
+        lmx[rb] = -INFINITY;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) lmx[rb] = fmaxf(lmx[rb], sacc[kb2][rb][e]);
+          for (int e = 0; e < 4; ++e) lmx[rb] = fmaxf(lmx[rb], sacc[kb2][rb][e]);
+      }
+    };
+    // Far tiles come after the near tiles, where every row met its own key
+    // (c = s > 0), so their rows' maxima are finite.  There the mask can wait
+    // for the raise below: if no entry, counted or not, outgrows its row's
+    // maximum by the margin, every exponent is at most 8 and an uncounted
+    // entry weighs 2^t * 0 = 0; only a chunk that triggers the raise is
+    // masked first.
+    constexpr bool DEFER = PL && KIND != KIND_NEAR;
+    if (!inside && !DEFER) mask();
+    row_max();
     // raise the running maximum only when some row outgrows it by the margin
     bool grow = false;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) grow = grow || lmx[rb] > Mrow[rb] + thr;
     if (__builtin_amdgcn_ballot_w64(grow)) {
+      if constexpr (DEFER) {
+        if (!inside) {
+          mask();
+          row_max();
+        }
+      }
       // until the wave's first raise every maximum is -inf and every sum
       // zero: that raise rescales nothing
       const bool rescale = started;
