@@ -142,6 +142,35 @@ def test_attention_matches_oracle_small(gpu, case):
     say(f"  max err {err:.3e}")
 
 
+LARGE_LOGIT_CASES = [
+    # B, Hq, Hkv, n, d, dtype, sigmas, s, causal (Q scaled by 16)
+    (1, 4, 2, 900, 64, "bf16", (1.5, 6.0, 40.0, 300.0), 20, True),
+    (1, 4, 2, 900, 64, "bf16", (1.5, 6.0, 40.0, 300.0), 20, False),
+    (1, 4, 2, 700, 128, "bf16", (2.0, 12.0, 90.0, 400.0), 20, True),
+    (1, 2, 2, 700, 128, "bf16", (2.0, 90.0), 40, False),    # two count chunks
+    (1, 2, 1, 500, 128, "f32", (3.0, 60.0), 8, True),
+    (1, 2, 1, 500, 64, "f32", (3.0, 60.0), 8, False),
+]
+
+
+@pytest.mark.parametrize("case", LARGE_LOGIT_CASES,
+                         ids=lambda c: f"H{c[1]}/{c[2]}n{c[3]}d{c[4]}{c[5]}s{c[7]}{'c' if c[8] else 'nc'}")
+def test_large_logits_raise_in_far_tiles(gpu, case):
+    """Q scaled by 16, so the logits spread over hundreds and chunks of the
+    far tiles raise the running maximum, also on entries whose count is 0
+    (a far chunk is masked only when it triggers a raise): every output is
+    finite and within the tolerances of the oracle."""
+    B, Hq, Hkv, n, d, dtype, sig, s, causal = case
+    say(f"large logits {case}")
+    (q, k, v), (q64, k64, v64) = _qkv_dev(B, Hq, Hkv, n, d, dtype, 21 + n, gpu, scale_q=16.0)
+    delta, u = oracle_hashes(13, sig, s, *P.draw_hashes(13, sig, s))
+    o = P.attention(q, k, v, sig, s, seed=13, causal=causal)
+    torch.cuda.synchronize()
+    ref = oracle_full(q64, k64, v64, delta, u, causal)
+    err = check_slices(to64(o), ref, dtype, where=str(case))
+    say(f"  max err {err:.3e}")
+
+
 @pytest.mark.parametrize("name", ["tiny", "small"])
 def test_workload_full_compare(gpu, name):
     W = synth.WORKLOADS[name]
