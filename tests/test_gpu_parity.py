@@ -142,6 +142,40 @@ def test_attention_matches_oracle_small(gpu, case):
     say(f"  max err {err:.3e}")
 
 
+def _random_cases(count, seed):
+    """Seeded random configurations: GQA ratios 1..8, odd n, s across the
+    hash-chunk boundaries, log-uniform widths 0.5..600, both dtypes and
+    head sizes, causal or not, Q scaled by 1, 2 or 4."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        hkv = int(rng.choice([1, 2]))
+        hq = hkv * int(rng.choice([1, 2, 4, 8]))
+        out.append((int(rng.choice([1, 2])), hq, hkv, int(rng.integers(1, 800)), int(rng.choice([64, 128])),
+                    str(rng.choice(["bf16", "f32"])),
+                    tuple(float(x) for x in np.exp(rng.uniform(np.log(0.5), np.log(600.0), size=hq))),
+                    int(rng.choice([1, 2, 5, 8, 13, 20, 31, 32, 33, 47, 64, 65, 90, 128])),
+                    bool(rng.integers(0, 2)), int(rng.integers(0, 2 ** 32)), float(rng.choice([1.0, 2.0, 4.0]))))
+    return out
+
+
+RANDOM_CASES = _random_cases(32, 2026)
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES,
+                         ids=lambda c: f"B{c[0]}H{c[1]}/{c[2]}n{c[3]}d{c[4]}{c[5]}s{c[7]}{'c' if c[8] else 'nc'}")
+def test_random_configurations_match_oracle(gpu, case):
+    B, Hq, Hkv, n, d, dtype, sig, s, causal, seed, scale = case
+    say(f"random configuration {case}")
+    (q, k, v), (q64, k64, v64) = _qkv_dev(B, Hq, Hkv, n, d, dtype, seed % 100000, gpu, scale_q=scale)
+    delta, u = oracle_hashes(seed, sig, s, *P.draw_hashes(seed, sig, s))
+    o = P.attention(q, k, v, sig, s, seed=seed, causal=causal)
+    torch.cuda.synchronize()
+    ref = oracle_full(q64, k64, v64, delta, u, causal)
+    err = check_slices(to64(o), ref, dtype, where=str(case))
+    say(f"  max err {err:.3e}")
+
+
 LARGE_LOGIT_CASES = [
     # B, Hq, Hkv, n, d, dtype, sigmas, s, causal (Q scaled by 16)
     (1, 4, 2, 900, 64, "bf16", (1.5, 6.0, 40.0, 300.0), 20, True),
