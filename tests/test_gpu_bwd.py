@@ -76,6 +76,41 @@ def test_lse_and_gradients_match_oracle(gpu, case):
     say(f"  worst rel err dQ {wq:.2e} dK {wk:.2e} dV {wv:.2e}")
 
 
+def _random_cases(count, seed):
+    """Seeded random configurations: GQA ratios 1..8, odd n, s across the
+    hash-chunk boundaries, log-uniform widths 0.5..600, d 64 and 128,
+    causal or not."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        hkv = int(rng.choice([1, 2]))
+        hq = hkv * int(rng.choice([1, 2, 4, 8]))
+        out.append((int(rng.choice([1, 2])), hq, hkv, int(rng.integers(1, 420)), int(rng.choice([64, 128])),
+                    tuple(float(x) for x in np.exp(rng.uniform(np.log(0.5), np.log(600.0), size=hq))),
+                    int(rng.choice([1, 3, 8, 20, 32, 33, 64, 65, 128])), bool(rng.integers(0, 2)),
+                    int(rng.integers(0, 2 ** 32))))
+    return out
+
+
+RANDOM_CASES = _random_cases(16, 4242)
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES,
+                         ids=lambda c: f"B{c[0]}H{c[1]}/{c[2]}n{c[3]}d{c[4]}s{c[6]}{'c' if c[7] else 'nc'}")
+def test_random_configurations_gradients(gpu, case):
+    B, Hq, Hkv, n, d, sig, s, causal, seed = case
+    say(f"backward random configuration {case}")
+    (q, k, v, do), (q64, k64, v64, do64) = _dev(B, Hq, Hkv, n, d, seed % 100000, gpu)
+    ldelta, lu, bins = P.sample_bins(seed, sig, s, n, device=gpu)
+    delta, u = oracle_hashes(seed, sig, s, ldelta, lu)
+    o, lse = P.attention_lse(q, k, v, bins, causal=causal, delta=ldelta)
+    dq, dk, dv = P.attention_bwd(q, k, v, o, do, lse, bins, causal=causal, delta=ldelta)
+    torch.cuda.synchronize()
+    gq, gk, gv = oracle.plsh_attention_grad(q64, k64, v64, do64, delta, u, causal)
+    say(f"  worst rel err dQ {_rel(to64(dq), gq, 'dQ'):.2e} dK {_rel(to64(dk), gk, 'dK'):.2e} "
+        f"dV {_rel(to64(dv), gv, 'dV'):.2e}")
+
+
 def test_gradients_mid_size_full_compare(gpu):
     B, Hq, Hkv, n, d, s = 1, 4, 2, 1024, 128, 20
     sig = synth.alibi_sigmas(Hq)
