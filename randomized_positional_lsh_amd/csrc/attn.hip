@@ -163,8 +163,9 @@ __device__ __forceinline__ void scatter_starts(const FwdArgs& A, int h, int r0, 
 }
 
 template <int D, bool BF, bool CAUSAL, int NCH, int MODE>
-// second bound: waves per SIMD, from the workgroups that fit a CU's LDS
-__global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 ? 1 : 2) * NW / 4) void fwd_kernel(FwdArgs A,
+// second bound: waves per SIMD, from the workgroups that fit a CU's LDS (fp32: one
+// workgroup per CU, so that its operands fit without spilling)
+__global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 || !BF ? 1 : 2) * NW / 4) void fwd_kernel(FwdArgs A,
                                                                                               HeadOrder ord,
                                                                                               HeadScale hsc) {
   using G = Geo<D, BF>;
