@@ -162,10 +162,21 @@ __device__ __forceinline__ void scatter_starts(const FwdArgs& A, int h, int r0, 
   }
 }
 
+// Workgroups per CU a build is compiled for: two where both fit a CU's LDS
+// and the operands fit 128 VGPRs, else one (up to 256 VGPRs): fp32 (its
+// operands spilled at d = 64) and the count-weighted d = 128, not causal,
+// two- and four-hash-chunk builds (spilled 4 and 26).  One workgroup
+// without spills was faster in each case.
 template <int D, bool BF, bool CAUSAL, int NCH, int MODE>
-// second bound: waves per SIMD, from the workgroups that fit a CU's LDS (fp32: one
-// workgroup per CU, so that its operands fit without spilling)
-__global__ __launch_bounds__(NT, (Geo<D, BF>::BIG + SMALL > 80 * 1024 || !BF ? 1 : 2) * NW / 4) void fwd_kernel(FwdArgs A,
+constexpr int fwd_wgs_per_cu() {
+  if (Geo<D, BF>::BIG + SMALL > 80 * 1024 || !BF) return 1;
+  if (MODE == MODE_PLSH && D == 128 && NCH >= 2 && !CAUSAL) return 1;
+  return 2;
+}
+
+template <int D, bool BF, bool CAUSAL, int NCH, int MODE>
+// second bound: waves per SIMD
+__global__ __launch_bounds__(NT, (fwd_wgs_per_cu<D, BF, CAUSAL, NCH, MODE>() * NW / 4)) void fwd_kernel(FwdArgs A,
                                                                                               HeadOrder ord,
                                                                                               HeadScale hsc) {
   using G = Geo<D, BF>;
