@@ -225,10 +225,16 @@ def kernel_times(run, reps, cold):
     work enqueued before, so the pair spans the kernel).  cold: a 512 MiB buffer is
     read (summed) on the same stream before every launch, outside the events,
     which evicts the L2 and the 256 MB last-level cache; the eviction only
-    reads, so no dirty lines of its own are written back during the launch."""
+    reads, so no dirty lines of its own are written back during the launch.
+    Untimed (eviction, launch) pairs come first: the first few dozen cold
+    launches after warm work run slower while the device settles into the
+    alternation (at the Mistral layer, whichever cold loop came first in a
+    process measured 183-185 us per launch, every later one 170-171)."""
     import torch
     scratch = torch.ones(128 << 20, dtype=torch.float32, device=run.q.device) if cold else None
-    for _ in range(3):
+    for _ in range(100 if cold else 3):
+        if scratch is not None:
+            scratch.sum()
         run.step()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in ev:
