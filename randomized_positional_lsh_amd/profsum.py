@@ -10,11 +10,21 @@
       (bench.py evicts the caches that way before its cold-cache launches)
       and the others.
 
-  python -m randomized_positional_lsh_amd.profsum util DIR OUT.md --cmd "..."
-      Unit utilisation of the count-weighted attention kernel from one --pmc
+  python -m randomized_positional_lsh_amd.profsum util DIR OUT.md --cmd "..." [--kernel K]
+      Unit utilisation of one kernel (default the count-weighted attention
+      kernel at head_dim 128, bf16, causal, one hash chunk) from one --pmc
       pass of GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES, SQ_ACTIVE_INST_VALU,
       SQ_LDS_IDX_ACTIVE and SQ_LDS_BANK_CONFLICT (means over its dispatches;
       GRBM_GUI_ACTIVE summed over the 8 XCDs, so divided by 8 for cycles).
+
+  python -m randomized_positional_lsh_amd.profsum waves DIR [DIR ...] OUT.md --cmd "..." --kernel K ...
+      Per-wave instruction counts and wave states of the named kernels
+      (substrings of the demangled name, e.g. "bwd_kernel<128, true, 1,
+      false>") from --pmc passes that each hold SQ_WAVES: SQ_INSTS_* over
+      SQ_WAVES, and SQ_ACTIVE_INST_ANY, SQ_WAIT_INST_ANY and SQ_WAIT_ANY as
+      shares of SQ_WAVE_CYCLES; means over dispatches per (kernel, grid).
+      Dispatches that directly follow a bin kernel (the two-launch step's
+      attention, which reads its plan records) are left out.
 
   python -m randomized_positional_lsh_amd.profsum traffic FETCH WRITE CFETCH CWRITE OUT.json \
           --workload mistral --kernel-sha SHA --copy-bytes N --cmd "..."
@@ -114,17 +124,17 @@ def stats(d: str, out: str, cmd: str, grid: int = 4096 * 512) -> None:
     print("\n".join(lines))
 
 
-def util(d: str, out: str, cmd: str, cus: int = 256, simds: int = 1024, xcds: int = 8) -> None:
+def util(d: str, out: str, cmd: str, kernel: str = MAIN, cus: int = 256, simds: int = 1024, xcds: int = 8) -> None:
     path = _one(os.path.join(d, "**", "*counter_collection.csv"))
     per: dict = {}
     for r in csv.DictReader(open(path)):
-        if MAIN in r["Kernel_Name"]:
+        if kernel in r["Kernel_Name"]:
             per.setdefault(r["Dispatch_Id"], {})[r["Counter_Name"]] = float(r["Counter_Value"])
     need = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_LDS_IDX_ACTIVE",
             "SQ_LDS_BANK_CONFLICT")
     rows = [v for v in per.values() if all(k in v for k in need)]
     if not rows:
-        raise ValueError(f"no dispatches of {MAIN} with counters {need} in {path}")
+        raise ValueError(f"no dispatches of {kernel} with counters {need} in {path}")
     m = {k: statistics.mean(v[k] for v in rows) for k in need}
     cyc = m["GRBM_GUI_ACTIVE"] / xcds
     res = [
@@ -134,11 +144,75 @@ def util(d: str, out: str, cmd: str, cus: int = 256, simds: int = 1024, xcds: in
         ("LDS busy (SQ_LDS_IDX_ACTIVE / (cycles x CUs))", m["SQ_LDS_IDX_ACTIVE"] / (cyc * cus)),
         ("LDS bank-conflict stalls (SQ_LDS_BANK_CONFLICT / (cycles x CUs))", m["SQ_LDS_BANK_CONFLICT"] / (cyc * cus)),
     ]
-    lines = ["# Unit utilisation of the attention kernel", "", f"Command: `{cmd}`", "",
-             f"Kernel: {MAIN}, {len(rows)} dispatches; cycles per dispatch (GRBM_GUI_ACTIVE / {xcds}): {cyc:.0f}.",
+    lines = [f"# Unit utilisation of {_short(kernel) or kernel}", "", f"Command: `{cmd}`", "",
+             f"Kernel: {kernel}, {len(rows)} dispatches; cycles per dispatch (GRBM_GUI_ACTIVE / {xcds}): {cyc:.0f}.",
              "", "| unit | share of cycles |", "|---|---|"]
     lines += [f"| {name} | {100 * v:.1f}% |" for name, v in res]
     lines += ["", f"Source: {os.path.basename(path)} (rocprofv3 --pmc, counters per dispatch)."]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+_WAVE_ROWS = [
+    ("vector instructions (SQ_INSTS_VALU, matrix included)", "SQ_INSTS_VALU"),
+    ("matrix instructions (SQ_INSTS_MFMA)", "SQ_INSTS_MFMA"),
+    ("transcendental fp32 (SQ_INSTS_VALU_TRANS_F32)", "SQ_INSTS_VALU_TRANS_F32"),
+    ("scalar ALU (SQ_INSTS_SALU)", "SQ_INSTS_SALU"),
+    ("scalar memory (SQ_INSTS_SMEM)", "SQ_INSTS_SMEM"),
+    ("LDS (SQ_INSTS_LDS)", "SQ_INSTS_LDS"),
+    ("branches (SQ_INSTS_BRANCH)", "SQ_INSTS_BRANCH"),
+]
+_STATE_ROWS = [
+    ("issuing (SQ_ACTIVE_INST_ANY)", "SQ_ACTIVE_INST_ANY"),
+    ("ready, not issued (SQ_WAIT_INST_ANY)", "SQ_WAIT_INST_ANY"),
+    ("waiting on dependencies (SQ_WAIT_ANY)", "SQ_WAIT_ANY"),
+]
+
+
+def waves(dirs: list[str], out: str, cmd: str, kernels: list[str]) -> None:
+    # (kernel, grid) -> dispatch -> counter -> value, over every pass
+    per: dict = {}
+    for d in dirs:
+        path = _one(os.path.join(d, "**", "*counter_collection.csv"))
+        rows = list(csv.DictReader(open(path)))
+        names = {int(r["Dispatch_Id"]): r["Kernel_Name"] for r in rows}
+        ids = sorted(names)
+        after_bins = {b for a, b in zip(ids, ids[1:]) if "bins_" in names[a]}
+        for r in rows:
+            i = int(r["Dispatch_Id"])
+            k = next((k for k in kernels if k in r["Kernel_Name"]), None)
+            if k is None or i in after_bins:
+                continue
+            key = (k, int(r["Grid_Size"]) // int(r["Workgroup_Size"]))
+            c = per.setdefault(key, {}).setdefault((d, i), {})
+            c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    lines = ["# Instructions and wave states per wave", "", f"Command: `{cmd}`", "",
+             "Means over dispatches of each counter divided by SQ_WAVES of the same dispatch; wave states as "
+             "shares of SQ_WAVE_CYCLES (quad-cycles per wave).", ""]
+    for (k, wgs), disp in sorted(per.items()):
+        vals: dict = {}
+        for c in disp.values():
+            if c.get("SQ_WAVES", 0.0) <= 0.0:
+                continue
+            for name, v in c.items():
+                if name != "SQ_WAVES":
+                    vals.setdefault(name, []).append(v / c["SQ_WAVES"])
+        if not vals:
+            continue
+        m = {name: statistics.mean(v) for name, v in vals.items()}
+        lines += [f"## {k}, {wgs} workgroups", "", "| per wave | value |", "|---|---|"]
+        for label, name in _WAVE_ROWS:
+            if name in m:
+                lines.append(f"| {label} | {m[name]:.0f} |")
+        if "SQ_WAVE_CYCLES" in m:
+            wc = m["SQ_WAVE_CYCLES"]
+            lines.append(f"| wave life, quad-cycles (SQ_WAVE_CYCLES) | {wc:.0f} |")
+            for label, name in _STATE_ROWS:
+                if name in m:
+                    lines.append(f"| {label} | {100 * m[name] / wc:.0f}% |")
+        lines.append("")
+    lines.append("Source: counter_collection.csv of each pass (rocprofv3 --pmc, counters per dispatch).")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -194,6 +268,11 @@ def main() -> None:
     c.add_argument("dir")
     c.add_argument("out")
     c.add_argument("--cmd", required=True)
+    c.add_argument("--kernel", default=MAIN)
+    w = sub.add_parser("waves")
+    w.add_argument("paths", nargs="+", help="pass directories, then the output file")
+    w.add_argument("--cmd", required=True)
+    w.add_argument("--kernel", action="append", required=True)
     b = sub.add_parser("traffic")
     for x in ("fetch", "write", "cfetch", "cwrite", "out"):
         b.add_argument(x)
@@ -204,8 +283,10 @@ def main() -> None:
     args = ap.parse_args()
     if args.cmd_name == "stats":
         stats(args.dir, args.out, args.cmd, args.grid)
+    elif args.cmd_name == "waves":
+        waves(args.paths[:-1], args.paths[-1], args.cmd, args.kernel)
     elif args.cmd_name == "util":
-        util(args.dir, args.out, args.cmd)
+        util(args.dir, args.out, args.cmd, args.kernel)
     else:
         traffic(args.fetch, args.write, args.cfetch, args.cwrite, args.out, args.workload, args.kernel_sha,
                 args.copy_bytes, args.cmd)
