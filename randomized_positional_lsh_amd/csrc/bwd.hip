@@ -548,14 +548,32 @@ __global__ __launch_bounds__(NT, 2) void bwd_kernel(BwdArgs A, BwdOrder ord) {
             }
           }
         }
-        // P and dS; the row of each element is own (dQ) or other (dK/dV)
+        // P and dS; the row of each element is own (dQ) or other (dK/dV).
+        // dK/dV: the LSE and D of the tile's rows 16 (2 kc + kb2) + 4 g + e;
+        // without the causal cut and at head_dim 128 the four rows of a lane
+        // come in one 16-byte read (causal, that read's registers push the
+        // build to the limit; at head_dim 64 it measured slower), elsewhere
+        // they are read one by one
+        constexpr bool WIDE = KEYSIDE && !CAUSAL && D == 128;
+        u32x4 lw[WIDE ? 2 : 1], dw[WIDE ? 2 : 1];
+        if constexpr (WIDE) {
+#pragma unroll
+          for (int kb2 = 0; kb2 < 2; ++kb2) {
+            const int r4 = 16 * (2 * kc + kb2) + 4 * g;
+            lw[kb2] = lds128_at(ya + 2 * G::TILE + 4 * r4);
+            dw[kb2] = lds128_at(ya + 2 * G::TILE + 256 + 4 * r4);
+          }
+        }
         float p[2][4], ds[2][4];
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             float l2, dr;
-            if constexpr (KEYSIDE) {
+            if constexpr (WIDE) {
+              l2 = __uint_as_float(lw[kb2][e]) * kLog2e;
+              dr = __uint_as_float(dw[kb2][e]);
+            } else if constexpr (KEYSIDE) {
               const int rr = 16 * (2 * kc + kb2) + 4 * g + e;  // row within the tile
               l2 = lds_f32_at(ya + 2 * G::TILE + 4 * rr) * kLog2e;
               dr = lds_f32_at(ya + 2 * G::TILE + 256 + 4 * rr);
