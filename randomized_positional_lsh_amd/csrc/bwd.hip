@@ -394,6 +394,12 @@ __global__ __launch_bounds__(NT, 2) void bwd_kernel(BwdArgs A, BwdOrder ord) {
     // before its phase, so that it does not sit beside the near-count
     // operand (or the other factor) in registers.
     u32x4 fl[NCH], fr[NCH];
+    // dQ at head_dim 128: the other side's bounds of the lane's slots
+    // 32 ch + 8 g + k, read with the own factors: a (left) or e2 (right).
+    // The dK/dV kernel has no registers for them and reads them per chunk,
+    // as do the head_dim 64 builds (where holding them measured slower).
+    constexpr bool HOIST = !KEYSIDE && D == 128;
+    int ob[HOIST ? NCH : 1][8];
     auto own_factors = [&](bool right, u32x4 (&f)[NCH]) {
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
@@ -402,6 +408,10 @@ __global__ __launch_bounds__(NT, 2) void bwd_kernel(BwdArgs A, BwdOrder ord) {
         for (int u2 = 0; u2 < 4; ++u2) {
           const u32x4 r0v = *reinterpret_cast<const u32x4*>(hp + 16 * (2 * u2));
           const u32x4 r1v = *reinterpret_cast<const u32x4*>(hp + 16 * (2 * u2 + 1));
+          if constexpr (HOIST) {
+            ob[ch][2 * u2] = static_cast<int>(right ? r0v[3] : r0v[0]);
+            ob[ch][2 * u2 + 1] = static_cast<int>(right ? r1v[3] : r1v[0]);
+          }
           f[ch][u2] = right ? ((own >= static_cast<int>(r0v[2]) ? 0x3F80u : 0u) |
                                (own >= static_cast<int>(r1v[2]) ? 0x3F800000u : 0u))
                             : ((own < static_cast<int>(r0v[1]) ? 0x3F80u : 0u) |
@@ -534,14 +544,20 @@ __global__ __launch_bounds__(NT, 2) void bwd_kernel(BwdArgs A, BwdOrder ord) {
               u32x4 af;
 #pragma unroll
               for (int u2 = 0; u2 < 4; ++u2) {
-                const u32x4 r0v = *reinterpret_cast<const u32x4*>(hp + 16 * (2 * u2));
-                const u32x4 r1v = *reinterpret_cast<const u32x4*>(hp + 16 * (2 * u2 + 1));
+                int b0, b1;
+                if constexpr (HOIST) {
+                  b0 = ob[ch][2 * u2];
+                  b1 = ob[ch][2 * u2 + 1];
+                } else {
+                  const u32x4 r0v = *reinterpret_cast<const u32x4*>(hp + 16 * (2 * u2));
+                  const u32x4 r1v = *reinterpret_cast<const u32x4*>(hp + 16 * (2 * u2 + 1));
+                  b0 = static_cast<int>(kind == 1 ? r0v[0] : r0v[3]);
+                  b1 = static_cast<int>(kind == 1 ? r1v[0] : r1v[3]);
+                }
                 if constexpr (kind == 1)  // left: [other >= a]
-                  af[u2] = (jo >= static_cast<int>(r0v[0]) ? 0x3F80u : 0u) |
-                           (jo >= static_cast<int>(r1v[0]) ? 0x3F800000u : 0u);
+                  af[u2] = (jo >= b0 ? 0x3F80u : 0u) | (jo >= b1 ? 0x3F800000u : 0u);
                 else  // right: [other < e2]
-                  af[u2] = (jo < static_cast<int>(r0v[3]) ? 0x3F80u : 0u) |
-                           (jo < static_cast<int>(r1v[3]) ? 0x3F800000u : 0u);
+                  af[u2] = (jo < b0 ? 0x3F80u : 0u) | (jo < b1 ? 0x3F800000u : 0u);
               }
               if constexpr (kind == 1) cc[kb2] = mfma_bf16(af, fl[ch], cc[kb2]);
               else cc[kb2] = mfma_bf16(af, fr[ch], cc[kb2]);
