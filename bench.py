@@ -40,8 +40,9 @@ Prints ONE JSON line.  Besides the contract fields it carries:
   backward     : a training step's attention on the same bins: the forward
                  with row normalisers (plpsh_attention_fwd_lse) and the
                  backward pass (plpsh_attention_bwd), each timed with HIP
-                 events; useful MFMA rate of the backward (5 products per
-                 counted pair against the forward's 2)
+                 events over 30 steps after 10 untimed ones (medians, and
+                 the backward's p10 / p90); useful MFMA rate of the backward
+                 (5 products per counted pair against the forward's 2)
   fixed_blocks : the deterministic fixed-blocks baseline (plpsh_fixed_blocks_fwd,
                  block b_h = round(2 sigma_h), the mean of Gamma(2, sigma_h))
   crossover    : PLSH vs dense ALiBi step times over n = 512 .. 131072
@@ -366,7 +367,7 @@ def literal(run, steps=10, warmup=3):
     return a.elapsed_time(b) / steps
 
 
-def backward(P, W, run, flops_fwd, steps=10, warmup=3):
+def backward(P, W, run, flops_fwd, steps=30, warmup=10):
     import numpy as np
     import torch
     q, k, v = run.q, run.k, run.v
@@ -392,15 +393,19 @@ def backward(P, W, run, flops_fwd, steps=10, warmup=3):
         P.attention_bwd(q, k, v, o, do, lse, bins, causal=W.causal, delta=delta, dq=dq, dk=dk, dv=dv, workspace=ws)
         c.record()
     torch.cuda.synchronize()
-    f_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
-    b_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    f_ms = float(np.median([a.elapsed_time(b) for a, b, _ in ev]))
+    bt = np.array([b.elapsed_time(c) for _, b, c in ev])
+    b_ms = float(np.median(bt))
     tflops = 2.5 * flops_fwd / (b_ms * 1e-3) / 1e12
     # algorithmic bytes: Q, O, dO, dQ (query-head sized), K, V, dK, dV (KV-head sized), LSE and D once each
     qsz = W.batch * W.heads_q * W.n * W.head_dim * 2
     kvsz = W.batch * W.heads_kv * W.n * W.head_dim * 2
     bwd_bytes = 4 * qsz + 4 * kvsz + 2 * 4 * W.batch * W.heads_q * W.n
     gbs = bwd_bytes / (b_ms * 1e-3) / 1e9
-    return {"fwd_lse_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4), "bwd_over_fwd": round(b_ms / f_ms, 2),
+    return {"fwd_lse_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
+            "bwd_ms_pct": {"p10": round(float(np.percentile(bt, 10)), 4), "p90": round(float(np.percentile(bt, 90)), 4),
+                           "mean": round(float(bt.mean()), 4)},
+            "bwd_over_fwd": round(b_ms / f_ms, 2),
             "train_tokens_per_s": round(W.batch * W.n / ((f_ms + b_ms) * 1e-3), 1),
             "bwd_useful_tflops": round(tflops, 2), "bwd_mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
             "bwd_algorithmic_bytes": bwd_bytes, "bwd_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
