@@ -26,8 +26,9 @@ P = pytest.importorskip("randomized_positional_lsh_amd")
 TOL = 2e-2
 
 
-def _dev(B, Hq, Hkv, n, d, seed, gpu):
+def _dev(B, Hq, Hkv, n, d, seed, gpu, scale_q=1.0):
     q, k, v = synth.qkv_numpy(B, Hq, Hkv, n, d, "bf16", seed, 2.0)
+    q = q * np.float32(scale_q)
     do = np.random.default_rng(seed + 1).standard_normal((B, Hq, n, d)).astype(np.float32)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(gpu).to(torch.bfloat16).contiguous()
     qt, kt, vt, dot = t(q), t(k), t(v), t(do)
@@ -74,6 +75,58 @@ def test_lse_and_gradients_match_oracle(gpu, case):
     wk = _rel(to64(dk), gk, "dK")
     wv = _rel(to64(dv), gv, "dV")
     say(f"  worst rel err dQ {wq:.2e} dK {wk:.2e} dV {wv:.2e}")
+
+
+LARGE_LOGIT_CASES = [
+    # B, Hq, Hkv, n, d, sigmas, s, causal (Q scaled by 16)
+    (1, 4, 2, 700, 128, (1.5, 6.0, 40.0, 300.0), 20, True),
+    (1, 4, 2, 700, 128, (1.5, 6.0, 40.0, 300.0), 20, False),
+    (1, 2, 1, 500, 64, (2.0, 90.0), 40, True),     # two hash chunks
+]
+
+
+def _max_uncounted_exponent(q64, k64, lse, delta, u, causal):
+    """Largest (S - LSE) log2(e) over the pairs whose count is 0: above 128
+    the backward's exponential of such a pair overflows fp32."""
+    B, Hq, n, d = q64.shape
+    grp = Hq // k64.shape[1]
+    worst = -np.inf
+    for b in range(B):
+        for h in range(Hq):
+            bins = [oracle.bin_values(a, c, n) for a, c in zip(delta[h], u[h])]
+            cnt = sum((bb[:, None] == bb[None, :]).astype(np.int32) for bb in bins)
+            if causal:
+                cnt = np.tril(cnt)
+            S = q64[b, h] @ k64[b, h // grp].T / math.sqrt(d)
+            x = (S - lse[b, h][:, None]) * math.log2(math.e)
+            worst = max(worst, x[cnt == 0].max(initial=-np.inf))
+    return worst
+
+
+@pytest.mark.parametrize("case", LARGE_LOGIT_CASES,
+                         ids=lambda c: f"H{c[1]}/{c[2]}n{c[3]}d{c[4]}s{c[6]}{'c' if c[7] else 'nc'}")
+def test_large_logits_gradients(gpu, case):
+    """Q scaled by 16: the logits spread over hundreds, so pairs whose count
+    is 0 have exponents far past fp32's range (checked from the oracle's
+    LSE); they must weigh 0, every gradient stays finite and within the
+    tolerance of the oracle."""
+    B, Hq, Hkv, n, d, sig, s, causal = case
+    say(f"backward large logits {case}")
+    (q, k, v, do), (q64, k64, v64, do64) = _dev(B, Hq, Hkv, n, d, 90 + n, gpu, scale_q=16.0)
+    ldelta, lu, bins = P.sample_bins(23, sig, s, n, device=gpu)
+    delta, u = oracle_hashes(23, sig, s, ldelta, lu)
+    o, lse = P.attention_lse(q, k, v, bins, causal=causal, delta=ldelta)
+    dq, dk, dv = P.attention_bwd(q, k, v, o, do, lse, bins, causal=causal, delta=ldelta)
+    torch.cuda.synchronize()
+    lse_ref = oracle.plsh_attention_lse(q64, k64, v64, delta, u, causal)
+    over = _max_uncounted_exponent(q64, k64, lse_ref, delta, u, causal)
+    say(f"  largest uncounted exponent {over:.1f}")
+    assert over > 128.0, "the case does not reach the overflow it is meant to test"
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all().item()
+    gq, gk, gv = oracle.plsh_attention_grad(q64, k64, v64, do64, delta, u, causal)
+    say(f"  worst rel err dQ {_rel(to64(dq), gq, 'dQ'):.2e} dK {_rel(to64(dk), gk, 'dK'):.2e} "
+        f"dV {_rel(to64(dv), gv, 'dV'):.2e}")
 
 
 def _random_cases(count, seed):
