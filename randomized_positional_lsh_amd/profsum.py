@@ -54,7 +54,8 @@ MAIN = "fwd_kernel<128, true, true, 1, 0>"
 EVICT = "reduce_kernel"  # torch's reduction kernel: bench.py's read-only cache eviction
 _MODES = {"0": "attention, count-weighted", "1": "dense exact ALiBi", "2": "one attention per hash"}
 _PLAIN = [
-    ("bins_kernel", "bin boundaries"),
+    ("bins_part_kernel", "bin boundaries, parts of 8192 positions"),
+    ("bins_kernel", "bin boundaries, one workgroup per hash"),
     ("rowdot_kernel", "backward D = <dO, O>"),
     ("rowmax_kernel", "error row maxima"),
     ("scan_local_kernel", "error product, tile scans"),
